@@ -1,0 +1,297 @@
+/*
+ * mla_oracle.c -- FP64 CPU oracle for MLA attention over a latent KV cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file; only the tests, the smoke check and the bench's CPU-baseline
+ * leg use it.  It shares no source with the HIP library.
+ *
+ * What it computes (plain definitions, no blocking, no fusion, no reordering):
+ *
+ *  - Latent KV row.  Every cached position holds one 576-wide row that serves
+ *    as the key; its first 512 entries serve as the value.  Keys and values are
+ *    projections into one shared latent space (InferenceX blog on Kimi K2.5,
+ *    section "PR #35850 修复了什么"), a row costs 576 FP8 bytes per position and
+ *    layer (Kimi K3 engineering report, section "缓存可复用，还要能一致地恢复"),
+ *    and query heads attend independently over the same history without
+ *    expanding it (same report, section "并行度必须适配真正的形状").
+ *    Absorbed-form MLA is therefore multi-query attention with key width 576
+ *    and value width 512; the 64 rotary dims are stored already rotated and
+ *    are treated like every other key dim.
+ *
+ *  - Softmax attention per query row (b, j, h):
+ *        s_t   = sigma * sum_d q_d k_{t,d}                t in visible set
+ *        m     = max_t s_t
+ *        l     = sum_t exp(s_t - m)
+ *        out_e = sum_t exp(s_t - m) v_{t,e} / l
+ *        lse   = m + ln l
+ *    An empty visible set gives out = 0 and lse = -inf.
+ *
+ *  - Merge of partial results by their normalisers (Kimi K3 report, section
+ *    "缓存可复用，还要能一致地恢复": position shards swap queries, attend over
+ *    their own positions and combine the pieces using each piece's normaliser):
+ *        M = max_p lse_p,  lse = M + ln sum_p exp(lse_p - M),
+ *        out = sum_p exp(lse_p - lse) out_p;  all lse_p = -inf gives 0 / -inf.
+ *
+ * Inputs are the raw bytes both paths consume: BF16 bit patterns for queries
+ * and BF16 caches, OCP FP8 E4M3FN codes plus one fp32 per-tensor scale for FP8
+ * caches.  Every input value is decoded exactly into a double; the product of
+ * an FP8 value (4 significant bits) and the fp32 scale (24 bits) is exact in a
+ * double, so the oracle sees the exact real dequantised key.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_DK 576 /* key width: 512 latent + 64 rotary */
+#define ORACLE_DV 512 /* value width: the latent part of the same row */
+
+/* ---- exact decoders ------------------------------------------------------ */
+
+/* OCP FP8 E4M3FN: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent 0 is subnormal (m * 2^-9); exponent 15 with mantissa 7 is NaN;
+ * there are no infinities, so the largest finite magnitude is 1.75 * 2^8. */
+double mla_oracle_fp8_e4m3fn_value(uint8_t code) {
+  int sign = code >> 7;
+  int e = (code >> 3) & 15;
+  int m = code & 7;
+  double mag;
+  if (e == 15 && m == 7) return NAN;
+  if (e == 0)
+    mag = ldexp((double)m, -9);
+  else
+    mag = ldexp(1.0 + m / 8.0, e - 7);
+  return sign ? -mag : mag;
+}
+
+/* BF16 is the upper half of an IEEE binary32. */
+double mla_oracle_bf16_value(uint16_t bits) {
+  uint32_t u = (uint32_t)bits << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+/* ---- key source: paged or contiguous latent rows ------------------------- */
+
+typedef struct {
+  const void* base;      /* [num_slots, 576] codes */
+  int fp8;               /* 1: FP8 E4M3FN codes, 0: BF16 bits */
+  double scale;          /* per-tensor dequant scale (1 for BF16) */
+  const int32_t* table;  /* block table row of this sequence, or NULL */
+  int block_size;        /* tokens per block when table != NULL */
+  const double* fp8_lut; /* 256 exact FP8 values */
+} kv_view;
+
+static const void* kv_row(const kv_view* v, long t) {
+  long slot = t;
+  if (v->table) slot = (long)v->table[t / v->block_size] * v->block_size + t % v->block_size;
+  return (const char*)v->base + (size_t)slot * ORACLE_DK * (v->fp8 ? 1 : 2);
+}
+
+static double kv_elem(const kv_view* v, const void* row, int d) {
+  if (v->fp8) return v->fp8_lut[((const uint8_t*)row)[d]] * v->scale;
+  return mla_oracle_bf16_value(((const uint16_t*)row)[d]);
+}
+
+/* Softmax attention of one query row over keys [begin, end) of one sequence.
+ * scores: scratch of at least (end - begin) doubles. */
+static void attend_row(const uint16_t* q_bits, const kv_view* kv, long begin, long end,
+                       double sigma, double* scores, double* out, double* lse) {
+  double q[ORACLE_DK];
+  for (int d = 0; d < ORACLE_DK; ++d) q[d] = mla_oracle_bf16_value(q_bits[d]);
+  for (int e = 0; e < ORACLE_DV; ++e) out[e] = 0.0;
+  if (end <= begin) {
+    *lse = -INFINITY;
+    return;
+  }
+  /* pass 1: scores and their maximum */
+  double m = -INFINITY;
+  for (long t = begin; t < end; ++t) {
+    const void* row = kv_row(kv, t);
+    double dot = 0.0;
+    for (int d = 0; d < ORACLE_DK; ++d) dot += q[d] * kv_elem(kv, row, d);
+    double s = sigma * dot;
+    scores[t - begin] = s;
+    if (s > m) m = s;
+  }
+  /* pass 2: normaliser and weighted sum of the value part of each row */
+  double l = 0.0;
+  for (long t = begin; t < end; ++t) {
+    double w = exp(scores[t - begin] - m);
+    l += w;
+    const void* row = kv_row(kv, t);
+    for (int e = 0; e < ORACLE_DV; ++e) out[e] += w * kv_elem(kv, row, e);
+  }
+  for (int e = 0; e < ORACLE_DV; ++e) out[e] /= l;
+  *lse = m + log(l);
+}
+
+static void fill_fp8_lut(double* lut) {
+  for (int c = 0; c < 256; ++c) lut[c] = mla_oracle_fp8_e4m3fn_value((uint8_t)c);
+}
+
+/*
+ * Decode / speculative verify over a paged latent cache.
+ *
+ * q            [B, P, H, 576] BF16 bits; query j of sequence b is context
+ *              position seq_lens[b] - P + j (the last P positions).
+ * kv           [num_blocks, block_size, 576] BF16 bits (kv_fp8 = 0) or
+ *              FP8 E4M3FN codes (kv_fp8 = 1) with value code * kv_scale.
+ * block_table  [B, max_blocks]: logical block i of sequence b lives in
+ *              physical block block_table[b * max_blocks + i].
+ * seq_lens     [B] context length including the P query positions.
+ * kv_begin     [B] or NULL (0): first key of the range this call covers.
+ * kv_end       [B] or NULL (seq_lens): end of the covered key range.
+ * Query j of sequence b sees keys t with
+ *              max(kv_begin, 0) <= t < min(kv_end, seq_lens - P + j + 1).
+ * rows         NULL: compute all B*P*H rows; else n_rows flat row indices
+ *              ((b * P + j) * H + h) to compute, in that order.
+ * out          [n, 512] doubles, lse [n] doubles, n = B*P*H or n_rows.
+ * Returns 0, or -1 on a bad argument.
+ */
+int mla_oracle_decode(const uint16_t* q, const void* kv, int kv_fp8, float kv_scale,
+                      const int32_t* block_table, int max_blocks, int block_size,
+                      const int32_t* seq_lens, const int32_t* kv_begin, const int32_t* kv_end,
+                      int B, int P, int H, float softmax_scale, const int64_t* rows,
+                      long n_rows, double* out, double* lse, int threads) {
+  if (!q || !kv || !block_table || !seq_lens || !out || !lse) return -1;
+  if (B < 0 || P < 1 || H < 1 || block_size < 1 || max_blocks < 1) return -1;
+  double lut[256];
+  fill_fp8_lut(lut);
+  long total = (long)B * P * H;
+  long n = rows ? n_rows : total;
+  long max_len = 0;
+  for (int b = 0; b < B; ++b)
+    if (seq_lens[b] > max_len) max_len = seq_lens[b];
+  const double sigma = (double)softmax_scale;
+  int bad = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#endif
+#pragma omp parallel reduction(| : bad)
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)(max_len > 0 ? max_len : 1));
+    if (!scores) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (long i = 0; i < n; ++i) {
+      long flat = rows ? rows[i] : i;
+      if (!scores || flat < 0 || flat >= total) {
+        bad = 1;
+        continue;
+      }
+      int j = (int)((flat / H) % P);
+      int b = (int)(flat / ((long)H * P));
+      kv_view v = {kv, kv_fp8, kv_fp8 ? (double)kv_scale : 1.0,
+                   block_table + (size_t)b * max_blocks, block_size, lut};
+      long begin = kv_begin ? kv_begin[b] : 0;
+      if (begin < 0) begin = 0;
+      long end = (long)seq_lens[b] - P + j + 1;
+      if (kv_end && kv_end[b] < end) end = kv_end[b];
+      attend_row(q + (size_t)flat * ORACLE_DK, &v, begin, end, sigma, scores,
+                 out + (size_t)i * ORACLE_DV, lse + i);
+    }
+    free(scores);
+  }
+  return bad ? -1 : 0;
+}
+
+/*
+ * Causal prefill over packed variable-length sequences.
+ *
+ * q          [T, H, 576] BF16 bits, kv [T, 576] BF16 bits or FP8 codes.
+ * cu_seqlens [B + 1]: sequence b owns tokens [cu_seqlens[b], cu_seqlens[b+1]).
+ * Token g of sequence b (cu_seqlens[b] <= g) sees keys cu_seqlens[b] .. g.
+ * tokens     NULL: all T tokens; else n_tokens global token indices, each
+ *            computed for all H heads, in that order.
+ * out        [n, H, 512] doubles, lse [n, H] doubles.
+ */
+int mla_oracle_prefill(const uint16_t* q, const void* kv, int kv_fp8, float kv_scale,
+                       const int32_t* cu_seqlens, int B, int H, float softmax_scale,
+                       const int64_t* tokens, long n_tokens, double* out, double* lse,
+                       int threads) {
+  if (!q || !kv || !cu_seqlens || !out || !lse || B < 0 || H < 1) return -1;
+  double lut[256];
+  fill_fp8_lut(lut);
+  long T = cu_seqlens[B];
+  long n = tokens ? n_tokens : T;
+  long max_len = 1;
+  for (int b = 0; b < B; ++b)
+    if (cu_seqlens[b + 1] - cu_seqlens[b] > max_len) max_len = cu_seqlens[b + 1] - cu_seqlens[b];
+  const double sigma = (double)softmax_scale;
+  int bad = 0;
+#ifdef _OPENMP
+  if (threads > 0) omp_set_num_threads(threads);
+#endif
+#pragma omp parallel reduction(| : bad)
+  {
+    double* scores = (double*)malloc(sizeof(double) * (size_t)max_len);
+    if (!scores) bad = 1;
+#pragma omp for schedule(dynamic, 1)
+    for (long r = 0; r < n * H; ++r) {
+      long i = r / H;
+      int h = (int)(r % H);
+      long g = tokens ? tokens[i] : i;
+      if (!scores || g < 0 || g >= T) {
+        bad = 1;
+        continue;
+      }
+      int b = 0;
+      while (b < B && cu_seqlens[b + 1] <= g) ++b;
+      kv_view v = {kv, kv_fp8, kv_fp8 ? (double)kv_scale : 1.0, NULL, 1, lut};
+      attend_row(q + ((size_t)g * H + h) * ORACLE_DK, &v, cu_seqlens[b], g + 1, sigma, scores,
+                 out + ((size_t)i * H + h) * ORACLE_DV, lse + (size_t)i * H + h);
+    }
+    free(scores);
+  }
+  return bad ? -1 : 0;
+}
+
+/*
+ * Merge of S partial results over disjoint key ranges by their normalisers.
+ * part_out [S, N, 512], part_lse [S, N]  ->  out [N, 512], lse [N].
+ */
+int mla_oracle_merge(const double* part_out, const double* part_lse, int S, long N,
+                     double* out, double* lse) {
+  if (!part_out || !part_lse || !out || !lse || S < 1 || N < 0) return -1;
+  for (long n = 0; n < N; ++n) {
+    double M = -INFINITY;
+    for (int s = 0; s < S; ++s) {
+      double x = part_lse[(size_t)s * N + n];
+      if (x > M) M = x;
+    }
+    for (int e = 0; e < ORACLE_DV; ++e) out[n * ORACLE_DV + e] = 0.0;
+    if (M == -INFINITY) {
+      lse[n] = -INFINITY;
+      continue;
+    }
+    double sum = 0.0;
+    for (int s = 0; s < S; ++s) {
+      double x = part_lse[(size_t)s * N + n];
+      if (x != -INFINITY) sum += exp(x - M);
+    }
+    double L = M + log(sum);
+    lse[n] = L;
+    for (int s = 0; s < S; ++s) {
+      double x = part_lse[(size_t)s * N + n];
+      if (x == -INFINITY) continue;
+      double w = exp(x - L);
+      const double* o = part_out + ((size_t)s * N + n) * ORACLE_DV;
+      for (int e = 0; e < ORACLE_DV; ++e) out[n * ORACLE_DV + e] += w * o[e];
+    }
+  }
+  return 0;
+}
+
+/* Number of OpenMP threads a parallel region would use (0 without OpenMP). */
+int mla_oracle_max_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 0;
+#endif
+}

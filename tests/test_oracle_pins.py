@@ -1,0 +1,412 @@
+"""Pins of the FP64 oracle to things other than itself (CPU only).
+
+* codecs: every FP8 E4M3FN code against torch's float8_e4m3fn, format spot values;
+  every BF16 pattern against torch's bfloat16;
+* brute force on tiny inputs: full-matrix float64 softmax(Q K^T) V with scipy's
+  logsumexp / softmax, and 50-digit mpmath for a handful of keys;
+* closed forms: zero query (mean of the visible values, lse = ln n), one visible
+  key (out = v exactly), identical keys (out = v, lse = s + ln n);
+* invariants the pages state: heads are independent (zero padding and head
+  repetition leave real heads unchanged), partial results merged by their
+  normalisers equal the whole, the history is shared by all heads;
+* paging, causality and scale invariants;
+* the pages' closed-form byte counts.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import logsumexp, softmax
+
+import mla_inputs as mi
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+SIGMA = mi.softmax_scale_for()
+
+
+# ---------------------------------------------------------------------------
+# independent decoders (torch) and a dense brute-force reference
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits):
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def fp8_to_f64(codes):
+    t = torch.from_numpy(np.ascontiguousarray(codes))
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def cache_rows_f64(cache: mi.PagedCache, b: int, lo: int, hi: int) -> np.ndarray:
+    """Dense float64 latent rows [hi - lo, 576] of sequence b gathered through its table."""
+    t = np.arange(lo, hi)
+    blk = cache.block_table[b, t // cache.block_size]
+    codes = cache.kv[blk, t % cache.block_size]
+    if cache.kv_dtype == "fp8":
+        return fp8_to_f64(codes) * float(cache.kv_scale)
+    return bf16_to_f64(codes)
+
+
+def brute_rows(qv: np.ndarray, K: np.ndarray, sigma: float):
+    """softmax(sigma Q K^T) V with V = K[:, :512], via scipy, in float64."""
+    if K.shape[0] == 0:
+        return np.zeros((qv.shape[0], 512)), np.full(qv.shape[0], -np.inf)
+    S = float(np.float32(sigma)) * (qv @ K.T)
+    return softmax(S, axis=1) @ K[:, :512], logsumexp(S, axis=1)
+
+
+def brute_decode(q_bits, cache, sigma, P, kv_begin=None, kv_end=None):
+    B, _, H, _ = q_bits.shape
+    out = np.zeros((B, P, H, 512))
+    lse = np.zeros((B, P, H))
+    for b in range(B):
+        L = int(cache.seq_lens[b])
+        for j in range(P):
+            lo = 0 if kv_begin is None else max(0, int(kv_begin[b]))
+            hi = L - P + j + 1
+            if kv_end is not None:
+                hi = min(hi, int(kv_end[b]))
+            K = cache_rows_f64(cache, b, lo, max(lo, hi))
+            o, s = brute_rows(bf16_to_f64(q_bits[b, j]), K, sigma)
+            out[b, j], lse[b, j] = o, s
+    return out, lse
+
+
+def tiny_decode(seed, lens, H=3, P=1, kv_dtype="bf16", block_size=16):
+    cache = mi.paged_cache(seed, lens, block_size, kv_dtype)
+    q = mi.normal_bf16_bits(seed, 3, (len(lens), P, H, 576))
+    return q, cache
+
+
+def run_decode(orc, q, cache, P=None, kv_begin=None, kv_end=None, sigma=SIGMA, rows=None):
+    return orc.decode(q, cache.kv, cache.kv_dtype == "fp8", cache.kv_scale, cache.block_table,
+                      cache.seq_lens, sigma, kv_begin=kv_begin, kv_end=kv_end, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# codecs
+# ---------------------------------------------------------------------------
+
+def test_fp8_codec_all_codes_match_torch():
+    ref = fp8_to_f64(np.arange(256, dtype=np.uint8))
+    got = np.array([oracle.fp8_e4m3fn_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    m = ~np.isnan(ref)
+    assert np.array_equal(ref[m], got[m])
+    assert np.array_equal(np.signbit(ref[m]), np.signbit(got[m]))
+
+
+def test_fp8_codec_format_spot_values():
+    spots = json.load(open(os.path.join(GOLDEN, "fp8_e4m3fn_spot_values.json")))["codes"]
+    for code, val in spots.items():
+        got = oracle.fp8_e4m3fn_value(int(code, 16))
+        if val == "nan":
+            assert math.isnan(got), code
+        else:
+            assert got == val, (code, got, val)
+
+
+def test_bf16_codec_all_patterns_match_torch():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = bf16_to_f64(bits)
+    for b in range(1 << 16):
+        g = oracle.bf16_value(b)
+        r = ref[b]
+        assert (math.isnan(g) and math.isnan(r)) or g == r, hex(b)
+
+
+# ---------------------------------------------------------------------------
+# brute force
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("P", [1, 3])
+def test_decode_matches_dense_bruteforce(kv_dtype, P):
+    lens = [5, 16, 33, 64]
+    q, cache = tiny_decode(11 + P, lens, H=4, P=P, kv_dtype=kv_dtype)
+    out, lse = run_decode(oracle, q, cache)
+    ref_out, ref_lse = brute_decode(q, cache, SIGMA, P)
+    assert np.max(np.abs(out - ref_out)) < 1e-12
+    assert np.max(np.abs(lse - ref_lse)) < 1e-12
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_decode_key_subrange_matches_bruteforce(kv_dtype):
+    lens = [40, 64, 17]
+    P = 2
+    q, cache = tiny_decode(23, lens, H=2, P=P, kv_dtype=kv_dtype, block_size=8)
+    kb = np.array([3, 0, 16], np.int32)
+    ke = np.array([30, 64, 17], np.int32)
+    out, lse = run_decode(oracle, q, cache, kv_begin=kb, kv_end=ke)
+    ref_out, ref_lse = brute_decode(q, cache, SIGMA, P, kb, ke)
+    fin = np.isfinite(ref_lse)
+    assert np.max(np.abs(out - ref_out)) < 1e-12
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.max(np.abs(lse[fin] - ref_lse[fin])) < 1e-12
+
+
+def test_decode_selected_rows_match_full():
+    q, cache = tiny_decode(31, [20, 45], H=3, P=2)
+    full_o, full_l = run_decode(oracle, q, cache)
+    rows = np.array([11, 0, 5, 7], np.int64)
+    o, l = run_decode(oracle, q, cache, rows=rows)
+    assert np.array_equal(o, full_o.reshape(-1, 512)[rows])
+    assert np.array_equal(l, full_l.reshape(-1)[rows])
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_prefill_matches_dense_bruteforce(kv_dtype):
+    lens = [5, 32, 3]
+    H = 3
+    w = mi.PrefillWorkload("tiny", lens, H, kv_dtype, seed=41)
+    d = mi.prefill_inputs(w)
+    out, lse = oracle.prefill(d["q"], d["kv"], kv_dtype == "fp8", d["kv_scale"], d["cu_seqlens"],
+                              SIGMA)
+    kvv = fp8_to_f64(d["kv"]) * d["kv_scale"] if kv_dtype == "fp8" else bf16_to_f64(d["kv"])
+    cu = d["cu_seqlens"]
+    for b in range(len(lens)):
+        for g in range(cu[b], cu[b + 1]):
+            K = kvv[cu[b]:g + 1]
+            o, s = brute_rows(bf16_to_f64(d["q"][g]), K, SIGMA)
+            assert np.max(np.abs(out[g] - o)) < 1e-12
+            assert np.max(np.abs(lse[g] - s)) < 1e-12
+
+
+def test_decode_matches_mpmath_50_digits():
+    mpmath = pytest.importorskip("mpmath")
+    mpmath.mp.dps = 50
+    lens = [1, 5, 8]
+    q, cache = tiny_decode(53, lens, H=2, P=1, kv_dtype="fp8", block_size=4)
+    out, lse = run_decode(oracle, q, cache)
+    sigma = mpmath.mpf(float(np.float32(SIGMA)))
+    for b, L in enumerate(lens):
+        K = cache_rows_f64(cache, b, 0, L)
+        for h in range(2):
+            qv = bf16_to_f64(q[b, 0, h])
+            s = [sigma * mpmath.fsum(mpmath.mpf(float(a)) * mpmath.mpf(float(c))
+                                     for a, c in zip(qv, K[t])) for t in range(L)]
+            m = max(s)
+            w = [mpmath.exp(x - m) for x in s]
+            l = mpmath.fsum(w)
+            ref_lse = m + mpmath.log(l)
+            assert abs(float(ref_lse) - lse[b, 0, h]) < 1e-14 * max(1.0, abs(float(ref_lse)))
+            for e in range(0, 512, 37):
+                ref = mpmath.fsum(w[t] * mpmath.mpf(float(K[t, e])) for t in range(L)) / l
+                assert abs(float(ref) - out[b, 0, h, e]) < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# closed forms
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_zero_query_gives_mean_of_visible_values(kv_dtype):
+    lens = [1, 9, 64, 100]
+    q, cache = tiny_decode(61, lens, H=2, P=1, kv_dtype=kv_dtype)
+    q[:] = 0
+    out, lse = run_decode(oracle, q, cache)
+    for b, L in enumerate(lens):
+        V = cache_rows_f64(cache, b, 0, L)[:, :512]
+        for h in range(2):
+            assert np.max(np.abs(out[b, 0, h] - V.mean(axis=0))) < 1e-13
+            assert lse[b, 0, h] == math.log(L)
+
+
+def test_single_visible_key_returns_its_value():
+    lens = [30, 64]
+    q, cache = tiny_decode(71, lens, H=3, P=1, kv_dtype="fp8")
+    kb = np.array([29, 10], np.int32)
+    ke = np.array([30, 11], np.int32)
+    out, lse = run_decode(oracle, q, cache, kv_begin=kb, kv_end=ke)
+    for b in range(2):
+        row = cache_rows_f64(cache, b, int(kb[b]), int(kb[b]) + 1)[0]
+        for h in range(3):
+            assert np.array_equal(out[b, 0, h], row[:512])
+            s = float(np.float32(SIGMA)) * math.fsum(bf16_to_f64(q[b, 0, h]) * row)
+            assert abs(lse[b, 0, h] - s) < 1e-12 * max(1.0, abs(s))
+
+
+def test_identical_keys_give_that_value():
+    lens = [48]
+    q, cache = tiny_decode(73, lens, H=2, P=1)
+    first = cache.kv[cache.block_table[0, 0], 0].copy()
+    for t in range(48):
+        cache.kv[cache.block_table[0, t // 16], t % 16] = first
+    out, lse = run_decode(oracle, q, cache)
+    row = bf16_to_f64(first)
+    for h in range(2):
+        assert np.array_equal(out[0, 0, h], row[:512])
+        s = float(np.float32(SIGMA)) * math.fsum(bf16_to_f64(q[0, 0, h]) * row)
+        assert abs(lse[0, 0, h] - (s + math.log(48))) < 1e-12
+
+
+def test_empty_range_gives_zero_and_minus_inf():
+    q, cache = tiny_decode(79, [20], H=2, P=1)
+    out, lse = run_decode(oracle, q, cache, kv_begin=np.array([20], np.int32))
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_partial_results_merged_by_lse_equal_the_whole(kv_dtype):
+    lens = [100, 37, 64]
+    P = 2
+    q, cache = tiny_decode(83, lens, H=3, P=P, kv_dtype=kv_dtype)
+    whole_o, whole_l = run_decode(oracle, q, cache)
+    cuts = [0, 13, 13, 50, 64, 99, 200]   # includes an empty piece and one past every end
+    po, pl = [], []
+    for a, c in zip(cuts[:-1], cuts[1:]):
+        kb = np.full(3, a, np.int32)
+        ke = np.full(3, c, np.int32)
+        o, l = run_decode(oracle, q, cache, kv_begin=kb, kv_end=ke)
+        po.append(o.reshape(-1, 512))
+        pl.append(l.reshape(-1))
+    mo, ml = oracle.merge(np.stack(po), np.stack(pl))
+    assert np.max(np.abs(mo - whole_o.reshape(-1, 512))) < 1e-12
+    assert np.max(np.abs(ml - whole_l.reshape(-1))) < 1e-12
+
+
+def test_merge_of_all_empty_pieces():
+    po = np.random.default_rng(0).standard_normal((3, 4, 512))
+    pl = np.full((3, 4), -np.inf)
+    o, l = oracle.merge(po, pl)
+    assert np.all(o == 0) and np.all(l == -np.inf)
+
+
+def test_merge_of_one_piece_is_identity():
+    rng = np.random.default_rng(1)
+    po = rng.standard_normal((1, 5, 512))
+    pl = rng.standard_normal((1, 5))
+    o, l = oracle.merge(po, pl)
+    assert np.max(np.abs(o - po[0])) < 1e-15 and np.max(np.abs(l - pl[0])) < 1e-15
+
+
+def test_zero_padded_heads_leave_real_heads_unchanged():
+    lens = [70, 128]
+    q, cache = tiny_decode(89, lens, H=12, P=4)
+    qp = np.zeros((2, 4, 16, 576), np.uint16)
+    qp[:, :, :12] = q
+    o12, l12 = run_decode(oracle, q, cache)
+    o16, l16 = run_decode(oracle, qp, cache)
+    assert np.array_equal(o16[:, :, :12], o12) and np.array_equal(l16[:, :, :12], l12)
+    # the padded heads see all-zero scores: the mean of the visible values
+    for b, L in enumerate(lens):
+        for j in range(4):
+            n = L - 4 + j + 1
+            V = cache_rows_f64(cache, b, 0, n)[:, :512]
+            assert np.max(np.abs(o16[b, j, 12:] - V.mean(axis=0))) < 1e-13
+            assert np.all(l16[b, j, 12:] == math.log(n))
+
+
+def test_repeated_heads_give_repeated_outputs():
+    q, cache = tiny_decode(97, [50], H=8, P=1)
+    qr = np.concatenate([q, q], axis=2)
+    o8, _ = run_decode(oracle, q, cache)
+    o16, _ = run_decode(oracle, qr, cache)
+    assert np.array_equal(o16[:, :, :8], o8) and np.array_equal(o16[:, :, 8:], o8)
+
+
+def test_history_shared_by_heads_is_not_expanded():
+    # one head alone equals that head inside a larger group: the history is per sequence
+    q, cache = tiny_decode(101, [77], H=6, P=1)
+    o6, _ = run_decode(oracle, q, cache)
+    for h in range(6):
+        o1, _ = run_decode(oracle, q[:, :, h:h + 1], cache)
+        assert np.array_equal(o1[:, :, 0], o6[:, :, h])
+
+
+def test_paging_layout_does_not_change_results():
+    lens = [77, 130]
+    q, c16 = tiny_decode(103, lens, H=2, P=2, block_size=16)
+    c64 = mi.paged_cache(103, lens, 64, "bf16", stream=9)
+    # copy the same logical rows into the second layout
+    for b, L in enumerate(lens):
+        for t in range(L):
+            c64.kv[c64.block_table[b, t // 64], t % 64] = c16.kv[c16.block_table[b, t // 16], t % 16]
+    a = run_decode(oracle, q, c16)
+    b2 = run_decode(oracle, q, c64)
+    assert np.array_equal(a[0], b2[0]) and np.array_equal(a[1], b2[1])
+
+
+def test_verify_position_equals_decode_on_its_prefix():
+    P = 4
+    q, cache = tiny_decode(107, [90, 65], H=3, P=P)
+    ov, lv = run_decode(oracle, q, cache)
+    for j in range(P):
+        c = mi.PagedCache(cache.kv, cache.kv_dtype, cache.kv_scale, cache.block_table,
+                          cache.seq_lens - P + j + 1, cache.block_size)
+        od, ld = run_decode(oracle, q[:, j:j + 1], c)
+        assert np.array_equal(od[:, 0], ov[:, j]) and np.array_equal(ld[:, 0], lv[:, j])
+
+
+def test_prefill_row_equals_decode_on_prefix_and_ignores_future_keys():
+    T, H = 40, 2
+    w = mi.PrefillWorkload("tiny", [T], H, "bf16", seed=109)
+    d = mi.prefill_inputs(w)
+    out, lse = oracle.prefill(d["q"], d["kv"], False, 1.0, d["cu_seqlens"], SIGMA)
+    kv = d["kv"].reshape(1, T, 576)
+    for i in [0, 1, 17, 39]:
+        o, l = oracle.decode(d["q"][i][None, None], kv, False, 1.0, np.zeros((1, 1), np.int32),
+                             np.array([i + 1], np.int32), SIGMA)
+        assert np.array_equal(o[0, 0], out[i]) and np.array_equal(l[0, 0], lse[i])
+    # prefill row 0 is exactly the first value row
+    assert np.array_equal(out[0, 0], bf16_to_f64(d["kv"][0])[:512])
+    kv2 = d["kv"].copy()
+    kv2[21:] ^= 0x1234
+    out2, lse2 = oracle.prefill(d["q"], kv2, False, 1.0, d["cu_seqlens"], SIGMA)
+    assert np.array_equal(out2[:21], out[:21]) and np.array_equal(lse2[:21], lse[:21])
+    assert not np.array_equal(out2[21:], out[21:])
+
+
+def test_power_of_two_query_scale_cancels():
+    q, cache = tiny_decode(113, [60], H=2, P=1)
+    q2 = mi.to_bf16_bits(bf16_to_f64(q).astype(np.float32) * 2.0)
+    a = run_decode(oracle, q, cache)
+    b = run_decode(oracle, q2, cache, sigma=float(np.float32(SIGMA) / np.float32(2.0)))
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_fp8_scale_equals_explicit_dequantisation():
+    # kv_scale = 2^-5: every code * scale is exactly a BF16 value, so a BF16 cache holding
+    # the dequantised rows must give identical results
+    lens = [50, 20]
+    q, cache = tiny_decode(127, lens, H=3, P=1, kv_dtype="fp8")
+    cache.kv_scale = 2.0 ** -5
+    deq = fp8_to_f64(cache.kv) * cache.kv_scale
+    bf = mi.PagedCache(mi.to_bf16_bits(deq.astype(np.float32)), "bf16", 1.0, cache.block_table,
+                       cache.seq_lens, cache.block_size)
+    a = run_decode(oracle, q, cache)
+    b = run_decode(oracle, q, bf)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_nan_poisoned_unused_slots_do_not_leak():
+    q, cache = tiny_decode(131, [3, 17, 31], H=2, P=2, kv_dtype="fp8")
+    assert np.any((cache.kv & 0x7F) == 0x7F)  # poison present
+    out, lse = run_decode(oracle, q, cache)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+# ---------------------------------------------------------------------------
+# the pages' closed forms
+# ---------------------------------------------------------------------------
+
+def test_latent_cache_bytes_match_pages():
+    g = json.load(open(os.path.join(GOLDEN, "pages_closed_forms.json")))
+    c = mi.paged_cache(1, [5], 64, "fp8")
+    row_bytes = c.kv.shape[-1] * c.kv.dtype.itemsize
+    assert row_bytes == g["latent_row_bytes_fp8"]["value"]
+    total = g["kv_bytes_142000_tokens_all_layers"]
+    assert total["tokens"] * row_bytes * g["mla_layers_kimi_k3"]["value"] == total["value"]
+    assert round(total["value"] / 1e9, 2) == 1.96
+    share = g["kv_bytes_142000_tokens_dcp8_share"]
+    assert total["value"] // share["shards"] == share["value"]
+    assert round(share["value"] / 1e6) == 245
