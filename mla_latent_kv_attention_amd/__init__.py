@@ -1,0 +1,245 @@
+"""MLA over a compressed latent KV cache on MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libmla.so`` (the C-ABI declared in ``include/mla.h``).
+It only marshals arguments: PyTorch supplies device memory and the current HIP
+stream; every step of the attention runs in the library's HIP kernels.  There is
+no other implementation behind these functions: if the library is missing they
+raise instead of computing anything.
+
+Entry points (same names as the C-ABI):
+  decode(q, kv_cache, block_table, seq_lens, ...)   one query position per sequence
+  verify(q, kv_cache, block_table, seq_lens, ...)   P query positions, causal among them
+  prefill(q, kv, cu_seqlens, ...)                   causal attention of packed sequences
+  merge_lse(part_out, part_lse, ...)                merge partials by log-sum-exp
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmla.so")
+
+HEAD_DIM_K = 576
+HEAD_DIM_V = 512
+MAX_ROWS = 64
+
+DTYPE_BF16 = 0
+DTYPE_FP8_E4M3 = 1
+DTYPE_FP32 = 2
+
+_STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype",
+           -3: "workspace missing or too small", -4: "HIP launch or query failed"}
+
+
+class MlaError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__("%s failed: %s (status %d)" % (fn, _STATUS.get(status, "?"), status))
+        self.status = status
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """The loaded HIP library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libmla.so is not built (%s); run mla_latent_kv_attention_amd/build.py" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.mla_verify.restype = I
+        lib.mla_verify.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, I, F, P, I, P, I, P, Z, P]
+        lib.mla_decode.restype = I
+        lib.mla_decode.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, F, P, I, P, I, P, Z, P]
+        lib.mla_prefill.restype = I
+        lib.mla_prefill.argtypes = [P, P, I, F, P, I, I, I, I, F, P, I, P, P]
+        lib.mla_merge_lse.restype = I
+        lib.mla_merge_lse.argtypes = [P, P, I, I, P, I, P, P]
+        lib.mla_decode_workspace_size.restype = Z
+        lib.mla_decode_workspace_size.argtypes = [I, I, I, I, I]
+        lib.mla_decode_num_splits.restype = I
+        lib.mla_decode_num_splits.argtypes = [I, I, I, I, I, I]
+        lib.mla_status_string.restype = ctypes.c_char_p
+        lib.mla_status_string.argtypes = [I]
+        lib.mla_version.restype = I
+        lib.mla_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MlaError(fn, status)
+
+
+def _kv_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return DTYPE_FP8_E4M3
+    raise TypeError("kv cache must be bfloat16, uint8 or float8_e4m3fn (FP8 E4M3FN codes)")
+
+
+def _out_dtype(d: torch.dtype) -> int:
+    if d == torch.float32:
+        return DTYPE_FP32
+    if d == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def _dev_i32(t: Optional[torch.Tensor], name: str, dev: torch.device):
+    if t is None:
+        return None
+    if t.dtype != torch.int32 or t.device != dev or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous int32 tensor on %s" % (name, dev))
+    return t
+
+
+def decode_num_splits(B: int, P: int, H: int, max_kv_len: int, num_splits: int = 0,
+                      num_cus: int = 0) -> int:
+    """Splits per sequence the call would use (num_cus = 0: the current device)."""
+    return library().mla_decode_num_splits(B, P, H, max_kv_len, num_splits, num_cus)
+
+
+def decode_workspace_size(B: int, P: int, H: int, max_kv_len: int, num_splits: int = 0) -> int:
+    return library().mla_decode_workspace_size(B, P, H, max_kv_len, num_splits)
+
+
+def verify(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+           seq_lens: torch.Tensor, *, softmax_scale: float, kv_scale: float = 1.0,
+           kv_begin: Optional[torch.Tensor] = None, kv_end: Optional[torch.Tensor] = None,
+           max_kv_len: Optional[int] = None, out_dtype: torch.dtype = torch.float32,
+           num_splits: int = 0, out: Optional[torch.Tensor] = None,
+           lse: Optional[torch.Tensor] = None, return_lse: bool = True,
+           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Speculative verify: q [B, P, H, 576] bf16 over a paged cache [blocks, block_size, 576].
+
+    Query j of sequence b is position seq_lens[b] - P + j and sees keys
+    kv_begin <= t < min(kv_end, seq_lens[b] - P + j + 1).  Returns (out [B, P, H, 512],
+    lse [B, P, H] fp32 or None).  ``max_kv_len`` (host int) bounds any sequence's key
+    range; when omitted it is read back from the device (a synchronisation).
+    """
+    lib = library()
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16:
+        raise TypeError("q must be [B, P, H, 576] bfloat16")
+    dev = q.device
+    B, P, H, _ = q.shape
+    q = q.contiguous()
+    if kv_cache.dim() != 3 or kv_cache.shape[-1] != HEAD_DIM_K or kv_cache.device != dev:
+        raise TypeError("kv_cache must be [num_blocks, block_size, 576] on the query's device")
+    kv_cache = kv_cache.contiguous()
+    kvd = _kv_dtype(kv_cache)
+    block_table = _dev_i32(block_table, "block_table", dev)
+    seq_lens = _dev_i32(seq_lens, "seq_lens", dev)
+    kv_begin = _dev_i32(kv_begin, "kv_begin", dev)
+    kv_end = _dev_i32(kv_end, "kv_end", dev)
+    if max_kv_len is None:
+        hi = seq_lens if kv_end is None else torch.minimum(seq_lens, kv_end)
+        lo = torch.zeros_like(hi) if kv_begin is None else kv_begin.clamp(min=0)
+        max_kv_len = int((hi - lo).clamp(min=0).max().item()) if B > 0 else 0
+    od = _out_dtype(out_dtype)
+    if out is None:
+        out = torch.empty((B, P, H, HEAD_DIM_V), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((B, P, H), dtype=torch.float32, device=dev)
+    ws_need = lib.mla_decode_workspace_size(B, P, H, max_kv_len, num_splits)
+    if workspace is None and ws_need > 0:
+        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+    st = lib.mla_verify(
+        _ptr(q), _ptr(kv_cache), kvd, float(kv_scale), _ptr(block_table),
+        block_table.shape[1], kv_cache.shape[1], _ptr(seq_lens), _ptr(kv_begin), _ptr(kv_end),
+        B, P, H, int(max_kv_len), float(softmax_scale), _ptr(out), od, _ptr(lse),
+        int(num_splits), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+        _stream(dev))
+    _check("mla_verify", st)
+    return out, lse
+
+
+def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+           seq_lens: torch.Tensor, **kw) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Decode: q [B, H, 576] bf16; returns (out [B, H, 512], lse [B, H] or None)."""
+    if q.dim() != 3:
+        raise TypeError("q must be [B, H, 576]")
+    out = kw.pop("out", None)
+    lse = kw.pop("lse", None)
+    o, l = verify(q.unsqueeze(1), kv_cache, block_table, seq_lens,
+                  out=None if out is None else out.unsqueeze(1),
+                  lse=None if lse is None else lse.unsqueeze(1), **kw)
+    return o.squeeze(1), (None if l is None else l.squeeze(1))
+
+
+def prefill(q: torch.Tensor, kv: torch.Tensor, cu_seqlens: torch.Tensor, *,
+            softmax_scale: float, kv_scale: float = 1.0, max_seqlen: Optional[int] = None,
+            out_dtype: torch.dtype = torch.bfloat16, out: Optional[torch.Tensor] = None,
+            lse: Optional[torch.Tensor] = None,
+            return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Causal prefill: q [T, H, 576] bf16, kv [T, 576]; cu_seqlens [B + 1] int32 on device."""
+    lib = library()
+    if q.dim() != 3 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16:
+        raise TypeError("q must be [T, H, 576] bfloat16")
+    dev = q.device
+    T, H, _ = q.shape
+    q = q.contiguous()
+    kv = kv.contiguous()
+    if kv.shape != (T, HEAD_DIM_K) or kv.device != dev:
+        raise TypeError("kv must be [T, 576] on the query's device")
+    cu = _dev_i32(cu_seqlens, "cu_seqlens", dev)
+    B = cu.numel() - 1
+    if max_seqlen is None:
+        max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if B > 0 else 0
+    od = _out_dtype(out_dtype)
+    if out is None:
+        out = torch.empty((T, H, HEAD_DIM_V), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    st = lib.mla_prefill(_ptr(q), _ptr(kv), _kv_dtype(kv), float(kv_scale), _ptr(cu), B, T,
+                         int(max_seqlen), H, float(softmax_scale), _ptr(out), od, _ptr(lse),
+                         _stream(dev))
+    _check("mla_prefill", st)
+    return out, lse
+
+
+def merge_lse(part_out: torch.Tensor, part_lse: torch.Tensor, *,
+              out_dtype: torch.dtype = torch.float32, out: Optional[torch.Tensor] = None,
+              lse: Optional[torch.Tensor] = None,
+              return_lse: bool = True) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Merge partials part_out [S, N, 512] fp32 / part_lse [S, N] fp32 by log-sum-exp."""
+    lib = library()
+    if part_out.dim() != 3 or part_out.shape[-1] != HEAD_DIM_V or part_out.dtype != torch.float32:
+        raise TypeError("part_out must be [S, N, 512] float32")
+    S, N, _ = part_out.shape
+    if part_lse.shape != (S, N) or part_lse.dtype != torch.float32:
+        raise TypeError("part_lse must be [S, N] float32")
+    dev = part_out.device
+    part_out = part_out.contiguous()
+    part_lse = part_lse.contiguous()
+    od = _out_dtype(out_dtype)
+    if out is None:
+        out = torch.empty((N, HEAD_DIM_V), dtype=out_dtype, device=dev)
+    if lse is None and return_lse:
+        lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    st = lib.mla_merge_lse(_ptr(part_out), _ptr(part_lse), S, N, _ptr(out), od, _ptr(lse),
+                           _stream(dev))
+    _check("mla_merge_lse", st)
+    return out, lse
+
+
+def default_softmax_scale(qk_dim: int = 192) -> float:
+    """1 / sqrt(qk_dim); 192 = 128 + 64 is the query-key width before absorption."""
+    return 1.0 / math.sqrt(qk_dim)

@@ -1,0 +1,92 @@
+// mla_device.h -- gfx950 device helpers shared by the MLA kernels.
+//
+// Register-fragment layouts below were checked on gfx950 hardware: for the
+// 16x16xK bf16 MFMA with K/16 values per lane, lane l holds A[l % 16][(K/4) *
+// (l / 16) + i], B[(K/4) * (l / 16) + i][l % 16], and the 16x16 f32 result
+// C[4 * (l / 16) + i][l % 16].  The LDS transpose read ds_read_b64_tr_b16
+// works on 16-lane groups: lane j of a group receives element (j % 4) of the
+// 8-byte chunk addressed by lane (4 * s + j / 4), for s = 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla_dev {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDK = 576;  // key width (512 latent + 64 rotary)
+constexpr int kDV = 512;  // value width (the latent part)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// S += A (16 x 32) * B (32 x 16), bf16 in, fp32 accumulate.
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// C += A (16 x 16) * B (16 x 16), bf16 in (as raw 16-bit lanes), fp32 accumulate.
+__device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Transposed 4 x 16-bit LDS read (see the layout note at the top).
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+}
+
+// Exact OCP E4M3FN -> bf16 for four codes packed in one dword (bytes 0..3).
+__device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x2& lo, bf16x2& hi) {
+  lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
+  hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+}
+
+// 16 FP8 codes -> two bf16x8 (codes 0..7, codes 8..15), exact.
+__device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, bf16x8& a, bf16x8& b) {
+  bf16x2 p0, p1, p2, p3, p4, p5, p6, p7;
+  fp8x4_to_bf16(w.x, p0, p1);
+  fp8x4_to_bf16(w.y, p2, p3);
+  fp8x4_to_bf16(w.z, p4, p5);
+  fp8x4_to_bf16(w.w, p6, p7);
+  a = (bf16x8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+  b = (bf16x8){p4.x, p4.y, p5.x, p5.y, p6.x, p6.y, p7.x, p7.y};
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float wave_max16x4(float v) {
+  // max over lanes {l, l ^ 16, l ^ 32, l ^ 48}
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum16x4(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+// Keep the compiler from moving LDS accesses across this point; lanes of one
+// wave exchange data through LDS around it.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+}  // namespace mla_dev

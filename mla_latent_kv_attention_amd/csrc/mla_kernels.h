@@ -1,0 +1,57 @@
+// mla_kernels.h -- launch interface between the C-ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla_impl {
+
+// Split-KV decode / verify over a paged latent cache.  One work-group per
+// (sequence, key split, 16-row block); four waves per work-group, each wave
+// streaming its own 16-token steps of the split.
+struct DecodeParams {
+  const uint16_t* q;           // [B, R, 576] bf16, R = P * H
+  const uint8_t* kv;           // [num_blocks, block_size, 576] bf16 or fp8 codes
+  const int32_t* block_table;  // [B, max_blocks]
+  const int32_t* seq_lens;     // [B]
+  const int32_t* kv_begin;     // [B] or null
+  const int32_t* kv_end;       // [B] or null
+  int max_blocks;
+  int block_size;              // multiple of 16
+  int B, P, H, R, RB;          // RB = ceil(R / 16)
+  int S;                       // splits per sequence
+  int chunk_tokens;            // tokens per split (multiple of 64); the last split takes the rest
+  int pairs;                   // B * S
+  float score_scale_log2;      // softmax_scale * kv_scale * log2(e)
+  float out_scale;             // kv_scale for fp8 caches, 1 for bf16
+  float* part_out;             // S > 1: [S, B * R, 512]
+  float* part_lse;             // S > 1: [S, B * R]
+  void* out;                   // S == 1: [B * R, 512] fp32 or bf16
+  int out_bf16;
+  float* lse;                  // S == 1: [B * R] or null
+};
+
+// Number of work-groups launch_decode_partial uses.
+int decode_grid_size(int pairs, int RB);
+
+hipError_t launch_decode_partial(const DecodeParams& p, bool kv_fp8, hipStream_t stream);
+
+hipError_t launch_merge(const float* part_out, const float* part_lse, int S, int N, void* out,
+                        int out_bf16, float* lse, hipStream_t stream);
+
+struct PrefillParams {
+  const uint16_t* q;           // [T, H, 576]
+  const uint8_t* kv;           // [T, 576] bf16 or fp8 codes
+  const int32_t* cu_seqlens;   // [B + 1]
+  int B, T, H, max_seqlen;
+  float score_scale_log2;
+  float out_scale;
+  void* out;                   // [T, H, 512]
+  int out_bf16;
+  float* lse;                  // [T, H] or null
+};
+
+hipError_t launch_prefill(const PrefillParams& p, bool kv_fp8, hipStream_t stream);
+
+}  // namespace mla_impl

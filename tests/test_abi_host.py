@@ -1,0 +1,146 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/mla.h declares,
+and its host-side logic (argument checks, split planner, workspace sizing) behaves as
+documented.  No compute call is made here: every call below is rejected, or returns,
+before anything is launched."""
+import ctypes
+import json
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import mla_latent_kv_attention_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from mla_latent_kv_attention_amd import build
+        build.build()
+    return m.library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ["mla_decode", "mla_verify", "mla_prefill", "mla_merge_lse",
+              "mla_decode_workspace_size", "mla_decode_num_splits", "mla_status_string",
+              "mla_version"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    assert lib.mla_status_string(0) == b"ok"
+    assert lib.mla_status_string(-3).startswith(b"workspace")
+    assert lib.mla_version() >= 100
+
+
+NULL = None
+
+
+def verify_args(**over):
+    a = dict(q=1, kv=1, kv_dtype=0, kv_scale=1.0, bt=1, max_blocks=4, block_size=64, sl=1,
+             kb=None, ke=None, B=2, P=1, H=12, max_kv_len=100, scale=0.07, out=1, out_dtype=2,
+             lse=None, splits=0, ws=None, ws_bytes=0, stream=None)
+    a.update(over)
+    # non-null pointers are never dereferenced: every call here fails a host check first
+    p = lambda v: None if v is None else ctypes.c_void_p(0x1000)
+    return [p(a["q"]), p(a["kv"]), a["kv_dtype"], a["kv_scale"], p(a["bt"]), a["max_blocks"],
+            a["block_size"], p(a["sl"]), p(a["kb"]), p(a["ke"]), a["B"], a["P"], a["H"],
+            a["max_kv_len"], a["scale"], p(a["out"]), a["out_dtype"], p(a["lse"]), a["splits"],
+            p(a["ws"]), a["ws_bytes"], a["stream"]]
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(P=0), -1),
+    (dict(H=0), -1),
+    (dict(B=-1), -1),
+    (dict(splits=-2), -1),
+    (dict(max_kv_len=-5), -1),
+    (dict(P=5, H=16), -2),          # 80 query rows per sequence: more than one work-group holds
+    (dict(kv_dtype=7), -2),
+    (dict(out_dtype=1), -2),        # FP8 is a cache format, not an output format
+    (dict(block_size=24), -1),
+    (dict(block_size=0), -1),
+    (dict(max_blocks=0), -1),
+    (dict(kv_dtype=1, kv_scale=0.0), -1),
+    (dict(kv_dtype=1, kv_scale=float("inf")), -1),
+    (dict(scale=float("nan")), -1),
+    (dict(q=None), -1),
+    (dict(kv=None), -1),
+    (dict(bt=None), -1),
+    (dict(sl=None), -1),
+    (dict(out=None), -1),
+])
+def test_verify_rejects_bad_arguments_before_launch(lib, over, status):
+    assert lib.mla_verify(*verify_args(**over)) == status
+
+
+def test_empty_batch_is_a_no_op(lib):
+    assert lib.mla_verify(*verify_args(B=0, q=None, kv=None, bt=None, sl=None, out=None)) == 0
+
+
+def test_merge_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p(0x1000)
+    assert lib.mla_merge_lse(P, P, 0, 4, P, 2, None, None) == -1
+    assert lib.mla_merge_lse(P, P, 2, -1, P, 2, None, None) == -1
+    assert lib.mla_merge_lse(P, P, 2, 4, P, 1, None, None) == -2
+    assert lib.mla_merge_lse(None, P, 2, 4, P, 2, None, None) == -1
+    assert lib.mla_merge_lse(None, None, 2, 0, None, 2, None, None) == 0
+
+
+def test_prefill_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p(0x1000)
+    assert lib.mla_prefill(P, P, 0, 1.0, P, 1, 16, 16, 0, 0.07, P, 0, None, None) == -1
+    assert lib.mla_prefill(P, P, 0, 1.0, P, 1, 16, 16, 65, 0.07, P, 0, None, None) == -2
+    assert lib.mla_prefill(P, P, 3, 1.0, P, 1, 16, 16, 12, 0.07, P, 0, None, None) == -2
+    assert lib.mla_prefill(P, P, 1, -1.0, P, 1, 16, 16, 12, 0.07, P, 0, None, None) == -1
+    assert lib.mla_prefill(None, P, 0, 1.0, P, 1, 16, 16, 12, 0.07, P, 0, None, None) == -1
+    assert lib.mla_prefill(None, None, 0, 1.0, None, 0, 0, 0, 12, 0.07, None, 0, None, None) == 0
+
+
+def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
+    """The pages' short verify: one sequence, 4 positions, 12 heads; 48 work-groups were
+    too few for the chip and 384 did better.  The split plan gives at least 384 work-groups
+    and at least one per CU once the history is long enough to split."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_closed_forms.json")))
+    sv = g["short_verify_workgroups"]
+    heads = sv["heads"]
+    assert heads * sv["tiled_width"] // sv["wide_tile_columns"] == sv["wide_tile_workgroups"]
+    assert heads * sv["tiled_width"] // sv["narrow_tile_columns"] == sv["narrow_tile_workgroups"]
+    rows = 4 * heads
+    row_blocks = -(-rows // 16)
+    for ctx in [8192, 32768, 142000]:
+        S = lib.mla_decode_num_splits(1, 4, heads, ctx, 0, 256)
+        assert S * row_blocks >= sv["narrow_tile_workgroups"]
+        assert S * row_blocks >= 256
+
+
+@pytest.mark.parametrize("B,P,H,L", [(1, 1, 12, 1024), (32, 1, 12, 16384), (4, 4, 12, 32768),
+                                     (4, 4, 16, 32768), (8, 1, 12, 17750), (3, 2, 8, 64)])
+def test_planner_splits_are_whole_rounds_and_cover_the_range(lib, B, P, H, L):
+    for cus in [80, 256, 304]:
+        S = lib.mla_decode_num_splits(B, P, H, L, 0, cus)
+        assert S >= 1
+        rounds = -(-L // 64)
+        assert S <= rounds
+        chunk_rounds = -(-rounds // S)
+        assert (S - 1) * chunk_rounds < rounds <= S * chunk_rounds
+
+
+def test_explicit_split_count_is_honoured(lib):
+    assert lib.mla_decode_num_splits(2, 1, 12, 1000, 7, 256) == 7
+    assert lib.mla_decode_num_splits(2, 1, 12, 10, 3, 256) == 3
+    assert lib.mla_decode_num_splits(2, 5, 16, 10, 3, 256) == -2
