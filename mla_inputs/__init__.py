@@ -87,13 +87,17 @@ def latent_rows(seed: int, stream: int, n_rows: int, kv_dtype: str):
             out[off:off + x.shape[0]] = to_bf16_bits(x)
         return out, 1.0
     if kv_dtype == "fp8":
+        x = np.empty((n_rows, DK), np.float32)
         amax = 0.0
-        for _, x in _chunked_normal(seed, stream, n_rows):
-            amax = max(amax, float(np.abs(x).max()))
+        for off, c in _chunked_normal(seed, stream, n_rows):
+            x[off:off + c.shape[0]] = c
+            amax = max(amax, float(np.abs(c).max()))
         scale = float(np.float32(amax / FP8_MAX))
-        out = np.empty((n_rows, DK), np.uint8)
-        for off, x in _chunked_normal(seed, stream, n_rows):
-            out[off:off + x.shape[0]] = to_fp8_codes(x, scale)
+        t = torch.from_numpy(x)
+        t.div_(torch.tensor(scale, dtype=torch.float32)).clamp_(-FP8_MAX, FP8_MAX)
+        out = t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        if np.any((out & 0x7F) == FP8_NAN_CODE):
+            raise ValueError("quantiser produced a NaN code")
         return out, scale
     raise ValueError("kv_dtype must be 'bf16' or 'fp8'")
 
