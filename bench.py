@@ -1,0 +1,258 @@
+#!/usr/bin/env python3
+"""Benchmark of MLA latent-KV decode on one MI355X, with roofline and CPU-oracle figures.
+
+A step is one pass of the decode hot path over one batch of the headline workload:
+32 sequences, 12 heads, one query each, per-sequence contexts uniform in [4096, 16384],
+FP8 E4M3 latent rows with a per-tensor scale in 64-token pages behind a shuffled block
+table (synthetic, seeded).  One step = the split-KV partial kernel + the LSE merge, both
+through the C-ABI; the inputs are resident in HBM before timing starts.  KV pools rotate
+over several copies so the 256 MB last-level cache cannot hold the one being read.
+
+Printed: ONE JSON line (metric, value = algorithmic KV-read GB/s of the whole step,
+roofline of the dominant kernel from HIP events on its stream, CPU oracle baseline,
+and the causal prefill figures the same metric names).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "MLA decode KV GB/s (% of HBM peak) + prefill tokens/s (% MFMA peak), 12 heads"
+DECODE_WORKLOAD = "decode_b32_h12_fp8_paged"
+PREFILL_WORKLOAD = "prefill_t32768_h12_bf16"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "mla_latent_kv_attention_amd", "csrc", name)
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_file: str, workload: str):
+    """Counter-derived HBM bytes per launch, if a summary for the current kernel source exists."""
+    path = os.path.join(PROFILE_DIR, "%s_pmc.json" % workload)
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+    except ValueError:
+        return None
+    if d.get("source_sha256_16") != source_hash(kernel_file):
+        return None  # the kernel changed since the counters were taken
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(q, cache, alg_bytes, min_seconds=10.0, max_reps=20):
+    """The FP64 oracle on the whole batch (every row), repeated until >= min_seconds."""
+    import oracle
+    import mla_inputs as mi
+    threads = oracle.max_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(q, cache.kv, cache.kv_dtype == "fp8", cache.kv_scale, cache.block_table,
+                      cache.seq_lens, mi.softmax_scale_for())
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or reps >= max_reps:
+            break
+    return {"value": alg_bytes * reps / el / 1e9, "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "the whole %s batch (all 384 query rows), %d pass(es), %.1f s of FP64 "
+                      "oracle time on %d threads" % (DECODE_WORKLOAD, reps, el, threads)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=3, help="KV pool copies cycled over")
+    ap.add_argument("--num-splits", type=int, default=0, help="0 = automatic split plan")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=5)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (position or head "
+              "sharding is a design note only); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import mla_inputs as mi
+    import mla_latent_kv_attention_amd as mla
+    from mla_latent_kv_attention_amd import accounting as acc
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import bf16_tensor, cache_to_device, check_lse, check_out
+
+    mla.library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # ---------------- decode workload ----------------
+    w = mi.WORKLOADS[DECODE_WORKLOAD]
+    log("generating", w.name)
+    d = mi.decode_inputs(w)
+    q_np, cache = d["q"], d["cache"]
+    B, P, H = q_np.shape[:3]
+    L = [int(x) for x in cache.seq_lens]
+    max_len = max(L)
+    kv0, bt, sl = cache_to_device(cache, dev)
+    pools = [kv0] + [kv0.clone() for _ in range(max(0, args.rotate - 1))]
+    q = bf16_tensor(q_np, dev).reshape(B, P, H, 576)
+    S = mla.decode_num_splits(B, P, H, max_len, args.num_splits)
+    N = B * P * H
+    part_out = torch.empty((S, N, 512), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((S, N), dtype=torch.float32, device=dev)
+    out = torch.empty((N, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    sigma = w.softmax_scale
+
+    def step(i):
+        kv = pools[i % len(pools)]
+        mla.verify_partials(q, kv, bt, sl, softmax_scale=sigma, kv_scale=cache.kv_scale,
+                            max_kv_len=max_len, num_splits=args.num_splits, part_out=part_out,
+                            part_lse=part_lse)
+
+    def merge():
+        mla.merge_lse(part_out, part_lse, out=out, lse=lse)
+
+    # parity on the timed buffers (every pool) before timing
+    import oracle
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(5).choice(N, 30, False)]))
+    ref_o, ref_l = oracle.decode(q_np, cache.kv, True, cache.kv_scale, cache.block_table,
+                                 cache.seq_lens, sigma, rows=rows.astype(np.int64))
+    idx = torch.from_numpy(rows).to(dev)
+    for i in range(len(pools)):
+        step(i)
+        merge()
+        torch.cuda.synchronize()
+        check_out(out[idx], ref_o, "decode out (pool %d)" % i)
+        check_lse(lse[idx], ref_l, "decode lse (pool %d)" % i)
+    log("parity ok on %d sampled rows, %d pools, %d splits" % (len(rows), len(pools), S))
+
+    alg_bytes = acc.decode_bytes(L, P, H, "fp8", out_bytes=4, block_size=cache.block_size)
+    alg_flops = acc.decode_flops(L, P, H)
+
+    for i in range(args.warmup):
+        step(i)
+        merge()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        e0, e1, e2 = ev[i]
+        e0.record(stream)
+        step(args.warmup + i)
+        e1.record(stream)
+        merge()
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    part_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    merge_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = alg_bytes / (part_ms.mean() * 1e-3) / 1e9
+    traffic = traffic_from_profile("mla_decode.hip", DECODE_WORKLOAD)
+    log("decode: %.1f us/step wall, partial kernel %.1f us (p10 %.1f, p90 %.1f), merge %.1f us"
+        % (ms_per_step * 1e3, part_ms.mean() * 1e3, np.percentile(part_ms, 10) * 1e3,
+           np.percentile(part_ms, 90) * 1e3, merge_ms.mean() * 1e3))
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8 kv / bf16 q / fp32 accumulate",
+        "data": "synthetic (seeded N(0,1), FP8 E4M3 per-tensor scale, shuffled 64-token pages)",
+        "config": {"workload": DECODE_WORKLOAD, "batch": B, "heads": H, "query_positions": P,
+                   "context": "uniform [4096, 16384]", "total_keys": int(sum(L)),
+                   "kv_dtype": "fp8_e4m3", "block_size": cache.block_size, "splits": S,
+                   "kv_pool_copies": len(pools), "algorithmic_bytes": alg_bytes,
+                   "algorithmic_flops": alg_flops},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_partial_kernel<fp8>",
+                     "kernel_us": round(float(part_ms.mean()) * 1e3, 2),
+                     "merge_us": round(float(merge_ms.mean()) * 1e3, 2)},
+    }
+
+    # ---------------- prefill (the metric's second half) ----------------
+    if not args.no_prefill:
+        pw = mi.WORKLOADS[PREFILL_WORKLOAD]
+        log("generating", pw.name)
+        pd = mi.prefill_inputs(pw)
+        T = pw.total_tokens
+        pq = bf16_tensor(pd["q"], dev).reshape(T, pw.heads, 576)
+        pkv = bf16_tensor(pd["kv"], dev).reshape(T, 576)
+        cu = torch.from_numpy(pd["cu_seqlens"]).to(dev)
+        pout = torch.empty((T, pw.heads, 512), dtype=torch.bfloat16, device=dev)
+        plse = torch.empty((T, pw.heads), dtype=torch.float32, device=dev)
+
+        def pstep():
+            mla.prefill(pq, pkv, cu, softmax_scale=pw.softmax_scale, max_seqlen=T,
+                        out_dtype=torch.bfloat16, out=pout, lse=plse)
+        pstep()
+        torch.cuda.synchronize()
+        toks = np.array([0, 1, 4095, T - 1], np.int64)
+        ro, rl = oracle.prefill(pd["q"], pd["kv"], False, 1.0, pd["cu_seqlens"],
+                                pw.softmax_scale, tokens=toks)
+        ti = torch.from_numpy(toks).to(dev)
+        check_out(pout[ti], ro, "prefill out")
+        check_lse(plse[ti], rl, "prefill lse")
+        pstep()
+        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.prefill_steps)]
+        torch.cuda.synchronize()
+        for a, b in pe:
+            a.record(stream)
+            pstep()
+            b.record(stream)
+        torch.cuda.synchronize()
+        pms = np.array([a.elapsed_time(b) for a, b in pe])
+        pflops = acc.prefill_flops(pw.seq_lens, pw.heads)
+        tflops = pflops / (pms.mean() * 1e-3) / 1e12
+        result["prefill"] = {
+            "workload": PREFILL_WORKLOAD, "tokens_per_s": round(T / (pms.mean() * 1e-3), 1),
+            "ms": round(float(pms.mean()), 3), "tflops": round(tflops, 1),
+            "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": pflops,
+            "kernel": "prefill_kernel<bf16>"}
+        log("prefill: %.2f ms, %.0f tok/s, %.1f TFLOP/s" % (pms.mean(), T / (pms.mean() * 1e-3),
+                                                          tflops))
+
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        result["cpu_baseline"] = cpu_baseline(q_np, cache, alg_bytes)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -9,6 +9,7 @@ raise instead of computing anything.
 Entry points (same names as the C-ABI):
   decode(q, kv_cache, block_table, seq_lens, ...)   one query position per sequence
   verify(q, kv_cache, block_table, seq_lens, ...)   P query positions, causal among them
+  verify_partials(...)                              verify's split stage without the merge
   prefill(q, kv, cu_seqlens, ...)                   causal attention of packed sequences
   merge_lse(part_out, part_lse, ...)                merge partials by log-sum-exp
 """
@@ -56,6 +57,8 @@ def library() -> ctypes.CDLL:
         P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.mla_verify.restype = I
         lib.mla_verify.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, I, F, P, I, P, I, P, Z, P]
+        lib.mla_verify_partials.restype = I
+        lib.mla_verify_partials.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, I, F, I, P, P, P]
         lib.mla_decode.restype = I
         lib.mla_decode.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, F, P, I, P, I, P, Z, P]
         lib.mla_prefill.restype = I
@@ -169,6 +172,41 @@ def verify(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
         _stream(dev))
     _check("mla_verify", st)
     return out, lse
+
+
+def verify_partials(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                    seq_lens: torch.Tensor, *, softmax_scale: float, kv_scale: float = 1.0,
+                    kv_begin: Optional[torch.Tensor] = None, kv_end: Optional[torch.Tensor] = None,
+                    max_kv_len: int, num_splits: int = 0,
+                    part_out: Optional[torch.Tensor] = None,
+                    part_lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """The split stage of verify alone: per-split (normalised out [S, B*P*H, 512], lse [S, B*P*H]).
+
+    merge_lse(part_out, part_lse) gives verify's result for the same arguments.
+    """
+    lib = library()
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16:
+        raise TypeError("q must be [B, P, H, 576] bfloat16")
+    dev = q.device
+    B, P, H, _ = q.shape
+    q = q.contiguous()
+    kv_cache = kv_cache.contiguous()
+    S = lib.mla_decode_num_splits(B, P, H, int(max_kv_len), int(num_splits), 0)
+    if S < 0:
+        raise MlaError("mla_decode_num_splits", S)
+    N = B * P * H
+    if part_out is None:
+        part_out = torch.empty((S, N, HEAD_DIM_V), dtype=torch.float32, device=dev)
+    if part_lse is None:
+        part_lse = torch.empty((S, N), dtype=torch.float32, device=dev)
+    st = lib.mla_verify_partials(
+        _ptr(q), _ptr(kv_cache), _kv_dtype(kv_cache), float(kv_scale),
+        _ptr(_dev_i32(block_table, "block_table", dev)), block_table.shape[1], kv_cache.shape[1],
+        _ptr(_dev_i32(seq_lens, "seq_lens", dev)), _ptr(_dev_i32(kv_begin, "kv_begin", dev)),
+        _ptr(_dev_i32(kv_end, "kv_end", dev)), B, P, H, int(max_kv_len), float(softmax_scale),
+        int(num_splits), _ptr(part_out), _ptr(part_lse), _stream(dev))
+    _check("mla_verify_partials", st)
+    return part_out, part_lse
 
 
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,

@@ -106,50 +106,68 @@ size_t mla_decode_workspace_size(int B, int P, int H, int max_kv_len, int num_sp
   return workspace_bytes_for(make_plan(B, P, H, max_kv_len, num_splits, current_cu_count()), B);
 }
 
+namespace {
+
+// Shared argument checks and parameter setup of mla_verify / mla_verify_partials.
+mla_status setup_decode(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
+                        const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                        const int32_t* seq_lens, const int32_t* kv_begin, const int32_t* kv_end,
+                        int B, int P, int H, int max_kv_len, float softmax_scale,
+                        int num_splits, mla_impl::DecodeParams* p, Plan* pl) {
+  if (B < 0 || P < 1 || H < 1 || max_kv_len < 0 || num_splits < 0) return MLA_E_INVAL;
+  if (kv_dtype != MLA_DTYPE_BF16 && kv_dtype != MLA_DTYPE_FP8_E4M3) return MLA_E_UNSUPPORTED;
+  if ((long)P * H > MLA_MAX_ROWS) return MLA_E_UNSUPPORTED;
+  if (block_size <= 0 || block_size % 16 != 0 || max_blocks_per_seq < 1) return MLA_E_INVAL;
+  if (!std::isfinite(softmax_scale)) return MLA_E_INVAL;
+  if (kv_dtype == MLA_DTYPE_FP8_E4M3 && !finite_positive(kv_scale)) return MLA_E_INVAL;
+  if (B > 0 && (!q || !kv_cache || !block_table || !seq_lens)) return MLA_E_INVAL;
+  const int cus = B > 0 ? current_cu_count() : 256;
+  if (cus <= 0) return MLA_E_LAUNCH;
+  *pl = make_plan(B, P, H, max_kv_len, num_splits, cus);
+  if (pl->S > 0 && (long)B * pl->S > 0x3fffffffL / (8 * pl->RB)) return MLA_E_UNSUPPORTED;
+  const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
+  const float kvs = fp8 ? kv_scale : 1.f;
+  *p = mla_impl::DecodeParams{};
+  p->q = static_cast<const uint16_t*>(q);
+  p->kv = static_cast<const uint8_t*>(kv_cache);
+  p->block_table = block_table;
+  p->seq_lens = seq_lens;
+  p->kv_begin = kv_begin;
+  p->kv_end = kv_end;
+  p->max_blocks = max_blocks_per_seq;
+  p->block_size = block_size;
+  p->B = B;
+  p->P = P;
+  p->H = H;
+  p->R = pl->R;
+  p->RB = pl->RB;
+  p->S = pl->S;
+  p->chunk_tokens = pl->chunk;
+  p->pairs = B * pl->S;
+  p->score_scale_log2 = softmax_scale * kvs * 1.4426950408889634f;
+  p->out_scale = kvs;
+  return MLA_OK;
+}
+
+}  // namespace
+
 mla_status mla_verify(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
                       const int32_t* block_table, int max_blocks_per_seq, int block_size,
                       const int32_t* seq_lens, const int32_t* kv_begin, const int32_t* kv_end,
                       int B, int P, int H, int max_kv_len, float softmax_scale, void* out,
                       int out_dtype, float* lse, int num_splits, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  if (B < 0 || P < 1 || H < 1 || max_kv_len < 0 || num_splits < 0) return MLA_E_INVAL;
-  if (kv_dtype != MLA_DTYPE_BF16 && kv_dtype != MLA_DTYPE_FP8_E4M3) return MLA_E_UNSUPPORTED;
   if (check_dtype_out(out_dtype) != MLA_OK) return MLA_E_UNSUPPORTED;
-  if ((long)P * H > MLA_MAX_ROWS) return MLA_E_UNSUPPORTED;
-  if (block_size <= 0 || block_size % 16 != 0 || max_blocks_per_seq < 1) return MLA_E_INVAL;
-  if (!std::isfinite(softmax_scale)) return MLA_E_INVAL;
-  if (kv_dtype == MLA_DTYPE_FP8_E4M3 && !finite_positive(kv_scale)) return MLA_E_INVAL;
+  if (B > 0 && !out) return MLA_E_INVAL;
+  mla_impl::DecodeParams p;
+  Plan pl;
+  mla_status st = setup_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
+                               block_size, seq_lens, kv_begin, kv_end, B, P, H, max_kv_len,
+                               softmax_scale, num_splits, &p, &pl);
+  if (st != MLA_OK) return st;
   if (B == 0) return MLA_OK;
-  if (!q || !kv_cache || !block_table || !seq_lens || !out) return MLA_E_INVAL;
-
-  const int cus = current_cu_count();
-  if (cus <= 0) return MLA_E_LAUNCH;
-  const Plan pl = make_plan(B, P, H, max_kv_len, num_splits, cus);
   const size_t need = workspace_bytes_for(pl, B);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_E_WORKSPACE;
-  if (pl.S > 0 && (long)B * pl.S > 0x3fffffffL / (8 * pl.RB)) return MLA_E_UNSUPPORTED;
-
-  const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
-  const float kvs = fp8 ? kv_scale : 1.f;
-  mla_impl::DecodeParams p{};
-  p.q = static_cast<const uint16_t*>(q);
-  p.kv = static_cast<const uint8_t*>(kv_cache);
-  p.block_table = block_table;
-  p.seq_lens = seq_lens;
-  p.kv_begin = kv_begin;
-  p.kv_end = kv_end;
-  p.max_blocks = max_blocks_per_seq;
-  p.block_size = block_size;
-  p.B = B;
-  p.P = P;
-  p.H = H;
-  p.R = pl.R;
-  p.RB = pl.RB;
-  p.S = pl.S;
-  p.chunk_tokens = pl.chunk;
-  p.pairs = B * pl.S;
-  p.score_scale_log2 = softmax_scale * kvs * 1.4426950408889634f;
-  p.out_scale = kvs;
   p.out = out;
   p.out_bf16 = out_dtype == MLA_DTYPE_BF16;
   p.lse = lse;
@@ -160,11 +178,40 @@ mla_status mla_verify(const void* q, const void* kv_cache, int kv_dtype, float k
     p.part_lse = reinterpret_cast<float*>(
         ws + align_up((size_t)pl.S * N * MLA_HEAD_DIM_V * sizeof(float)));
   }
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (mla_impl::launch_decode_partial(p, fp8, st) != hipSuccess) return MLA_E_LAUNCH;
+  hipStream_t stm = static_cast<hipStream_t>(stream);
+  const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
+  if (mla_impl::launch_decode_partial(p, fp8, stm) != hipSuccess) return MLA_E_LAUNCH;
   if (pl.S > 1 &&
-      mla_impl::launch_merge(p.part_out, p.part_lse, pl.S, N, out, p.out_bf16, lse, st) !=
+      mla_impl::launch_merge(p.part_out, p.part_lse, pl.S, N, out, p.out_bf16, lse, stm) !=
           hipSuccess)
+    return MLA_E_LAUNCH;
+  return MLA_OK;
+}
+
+mla_status mla_verify_partials(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
+                               const int32_t* block_table, int max_blocks_per_seq,
+                               int block_size, const int32_t* seq_lens, const int32_t* kv_begin,
+                               const int32_t* kv_end, int B, int P, int H, int max_kv_len,
+                               float softmax_scale, int num_splits, float* part_out,
+                               float* part_lse, void* stream) {
+  if (B > 0 && (!part_out || !part_lse)) return MLA_E_INVAL;
+  mla_impl::DecodeParams p;
+  Plan pl;
+  mla_status st = setup_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
+                               block_size, seq_lens, kv_begin, kv_end, B, P, H, max_kv_len,
+                               softmax_scale, num_splits, &p, &pl);
+  if (st != MLA_OK) return st;
+  if (B == 0) return MLA_OK;
+  if (pl.S == 1) {  // one split: the kernel writes its normalised rows directly
+    p.out = part_out;
+    p.out_bf16 = 0;
+    p.lse = part_lse;
+  } else {
+    p.part_out = part_out;
+    p.part_lse = part_lse;
+  }
+  const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
+  if (mla_impl::launch_decode_partial(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_E_LAUNCH;
   return MLA_OK;
 }

@@ -1,0 +1,341 @@
+// mla_prefill.hip -- causal MLA prefill (absorbed form) for gfx950.
+//
+// Every query row is a (token, head) pair; the heads of a token share the
+// token's latent rows and its causal limit.  The slow 12-head case on the
+// pages was one attention kernel that only had fast shapes for 4, 8 or
+// multiples of 16 heads (article on Kimi K3 on MI355X, section
+// "首Token等待优化：简单补零解决大问题"); here rows are simply (token, head)
+// pairs, so any head count tiles the same way.
+//
+// Work decomposition.  A work-group owns 128 consecutive query rows of one
+// sequence; each of its four waves owns 32 of them, with the waves' Q^T
+// fragments held in registers for the whole key loop (36 x 8 bf16 per lane).
+// The work-group walks the sequence's keys in 32-token tiles up to its last
+// row's token; each tile is staged once in LDS (bf16, padded rows; fp8 caches
+// widened exactly on the way in) with the next tile's loads in flight, and
+// read by all four waves:
+//   S^T[32 tokens x 32 rows] = K Q^T           36 MFMA 32x32x16 (A from LDS)
+//   causal mask, online softmax (running max moved only when it trails by > 2^8)
+//   O^T[512 x 32 rows] += V^T P^T               32 MFMA 32x32x16 (A = V^T read
+//                                               with ds_read_b64_tr_b16, B = P^T
+//                                               straight from the score registers)
+// Work-groups are launched longest-first (the last rows of a sequence see the
+// most keys), and consecutive ids fan out over the 8 XCDs, so every XCD works
+// on a mix of long and short rows that all stream the same leading key tiles.
+#include "mla_device.h"
+#include "mla_kernels.h"
+
+namespace mla_impl {
+using namespace mla_dev;
+
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kRowsPerWg = 128;
+constexpr int kRowsPerWave = 32;
+constexpr int kTile = 32;                        // key tokens per tile
+constexpr int kKSteps = 36;                      // 576 / 16
+constexpr int kRowBytes = 2 * kDK;               // 1152: one bf16 latent row
+constexpr int kPRowChunks = kRowBytes / 16 + 1;  // 73 16-byte chunks: 72 of data + 1 pad
+constexpr int kPRow = 8 * kPRowChunks;           // padded LDS row (bf16 elements)
+constexpr int kTileElems = kTile * kPRow;
+constexpr int kDmaPerWave = 10;                  // 4 waves x 10 x 1 KB cover a padded tile
+constexpr int kSlotBytes = 4 * kDmaPerWave * 1024;
+constexpr int kRing = 3;                         // bf16 tiles in flight / in use
+constexpr float kSlack = 8.0f;
+
+static_assert(kTile * kPRowChunks <= 4 * kDmaPerWave * 64, "DMA slots must cover a tile");
+
+// One 16-byte global -> LDS copy per lane, no VGPR staging: lane l reads
+// base + voff and lands at LDS byte lds_base + 16 l.  Issued through asm so the
+// compiler does not fence every later LDS read behind all outstanding loads; the
+// kernel waits for its own copies with explicit vmcnt waits and a barrier.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory", "m0");
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits 3:0,
+// vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their no-wait maxima).
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(kN >= 0 && kN < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+// Copy key tile [tok0, tok0 + 32) of a sequence into an LDS slot laid out as
+// 32 padded rows of 73 chunks.  Chunk positions past the tile land in the slot's
+// slack; pad chunks and rows past the sequence end get real (masked) rows.
+// seq_kv points at the sequence's first latent row.
+__device__ __forceinline__ void dma_tile(const uint8_t* seq_kv, int len, int tok0, uint32_t slot,
+                                         int wave, int lane) {
+  // keep the per-lane chunk coordinates out of loop-invariant code motion: ten
+  // of them held across the key loop would cost 20 VGPRs
+  int l = lane;
+  asm volatile("" : "+v"(l));
+#pragma unroll
+  for (int i = 0; i < kDmaPerWave; ++i) {
+    const int inst = wave + 4 * i;
+    const int pos = 64 * inst + l;
+    int row = pos / kPRowChunks, pc = pos - row * kPRowChunks;
+    if (row >= kTile) row = kTile - 1;
+    if (pc == kPRowChunks - 1) pc = 0;
+    const int t = min(tok0 + row, len - 1);
+    dma16(seq_kv, (uint32_t)(t * kRowBytes + 16 * pc), slot + 1024 * inst);
+  }
+}
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// FP8 tiles go through registers: 16 codes per 16-byte load, widened exactly to
+// bf16 on the way into the same padded LDS layout.
+struct Fp8Stage {
+  static constexpr int kRowChunks = kDK / 16;  // 36
+  static constexpr int kTotal = kTile * kRowChunks;
+  static constexpr int kChunks = (kTotal + 255) / 256;
+  u32x4 r[kChunks];
+
+  __device__ __forceinline__ void load(const uint8_t* kv, int seq_start, int len, int tok0,
+                                       int tid) {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const int c = tid + 256 * k;
+      if (c < kTotal) {
+        const int row = c / kRowChunks, cc = c % kRowChunks;
+        const int t = min(tok0 + row, len - 1);  // rows past the sequence end are masked
+        r[k] = *(const u32x4*)(kv + ((size_t)(seq_start + t) * kRowChunks + cc) * 16);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* buf, int tid) const {
+#pragma unroll
+    for (int k = 0; k < kChunks; ++k) {
+      const int c = tid + 256 * k;
+      if (c < kTotal) {
+        const int row = c / kRowChunks, cc = c % kRowChunks;
+        bf16x8 lo, hi;
+        fp8x16_to_bf16(r[k], lo, hi);
+        *(bf16x8*)(buf + row * kPRow + 16 * cc) = lo;
+        *(bf16x8*)(buf + row * kPRow + 16 * cc + 8) = hi;
+      }
+    }
+  }
+};
+
+// acc *= s for a 16-register MFMA accumulator kept in AGPRs: each element is read
+// into a VGPR, scaled and written back, so the accumulator keeps its register
+// class across the key loop (a plain multiply would move all 256 accumulator
+// values through VGPRs on every iteration).
+__device__ __forceinline__ void scale_acc(f32x16& acc, float s) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = acc[i];
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1"
+        : "+a"(x), "=&v"(t)
+        : "v"(s));
+    acc[i] = x;
+  }
+}
+
+template <bool kFp8>
+__global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) {
+  // bf16: a ring of 3 DMA slots (120 KB); fp8: two register-staged tiles (73 KB)
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kFp8 ? 2 * kTileElems : kRing * kSlotBytes / 2];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31;   // query row within the wave (B / C column)
+  const int g = lane >> 5;   // k-group (A, B) / row group of 4 (C)
+
+  // ---- work-group -> (sequence, row block), longest first within a sequence
+  int id = blockIdx.x;
+  int b = 0, len = 0, seq_start = 0, blk = -1;
+  for (; b < p.B; ++b) {
+    seq_start = p.cu_seqlens[b];
+    len = p.cu_seqlens[b + 1] - seq_start;
+    const int nb = (len * p.H + kRowsPerWg - 1) / kRowsPerWg;
+    if (id < nb) {
+      blk = nb - 1 - id;
+      break;
+    }
+    id -= nb;
+  }
+  if (blk < 0) return;
+  const int rows = len * p.H;
+  const int row0 = blk * kRowsPerWg;
+  const int wg_last_tok = min(len - 1, (row0 + kRowsPerWg - 1) / p.H);
+  const int n_tiles = wg_last_tok / kTile + 1;
+
+  // ---- this lane's query row and its Q^T fragments (B operand, 8 dims per k-step)
+  const int r = row0 + kRowsPerWave * wave + n;
+  const bool row_ok = r < rows;
+  const int tq = row_ok ? r / p.H : -1;  // causal limit: keys 0 .. tq
+  bf16x8 qf[kKSteps];
+  {
+    const uint16_t* qrow = p.q + ((size_t)seq_start * p.H + (row_ok ? r : 0)) * kDK + 8 * g;
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      bf16x8 v = *(const bf16x8*)(qrow + 16 * kk);
+      qf[kk] = row_ok ? v : (bf16x8){};
+    }
+  }
+  // retire the query loads here: a wait the compiler would otherwise place at
+  // their first use inside the key loop would also drain the tile copies in flight
+  wait_vmcnt<0>();
+
+  f32x16 acc[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = (f32x16){};
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // per-lane LDS offsets (elements) inside a tile
+  const int a_off = n * kPRow + 8 * g;  // K fragment: token n, dims 16 kk + 8 g
+  const int v_tok = 4 * g + ((lane & 15) >> 2);
+  const int v_off = v_tok * kPRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  // Rows whose token precedes the whole tile are fully masked (their P is 0);
+  // they still run the MFMAs: an early exit here would split the accumulator's
+  // live range and cost far more than the few skipped diagonal tiles.
+  auto compute = [&](const uint16_t* buf, int kt) {
+    {
+      // groups of 6 k-steps: bounds how many K fragments the scheduler keeps in flight
+      f32x16 sc = {};
+#pragma unroll
+      for (int k6 = 0; k6 < kKSteps; k6 += 6) {
+#pragma unroll
+        for (int kk = k6; kk < k6 + 6; ++kk)
+          sc = mfma_32x32x16(*(const bf16x8*)(buf + a_off + 16 * kk), qf[kk], sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // lane (n, g) holds tokens kt*32 + 8 (i/4) + 4 g + i%4 of row n
+      float sv[16];
+      float cm = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int t = kt * kTile + 8 * (i >> 2) + 4 * g + (i & 3);
+        sv[i] = (t <= tq) ? sc[i] * p.score_scale_log2 : -INFINITY;
+        cm = fmaxf(cm, sv[i]);
+      }
+      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      const float mn = fmaxf(m_run, cm);
+      const bool need = mn > m_run + kSlack;
+      if (__builtin_amdgcn_ballot_w64(need)) {
+        const float alpha = need ? fast_exp2(m_run - mn) : 1.f;
+        if (need) m_run = mn;
+        l_run *= alpha;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) scale_acc(acc[i], alpha);
+      }
+      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      float pv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        pv[i] = fast_exp2(sv[i] - mref);
+        l_run += pv[i];
+      }
+      // k-slot 8 g + s of k-step j holds token 16 j + 8 (s / 4) + 4 g + s % 4: exactly
+      // the score values i = 8 j + s this lane already has
+      bf16x8 pf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        pf[j] = (bf16x8){(__bf16)pv[8 * j + 0], (__bf16)pv[8 * j + 1], (__bf16)pv[8 * j + 2],
+                         (__bf16)pv[8 * j + 3], (__bf16)pv[8 * j + 4], (__bf16)pv[8 * j + 5],
+                         (__bf16)pv[8 * j + 6], (__bf16)pv[8 * j + 7]};
+#pragma unroll
+      for (int mb = 0; mb < 16; ++mb) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const uint16_t* src = buf + v_off + (16 * j) * kPRow + 32 * mb;
+          const i16x4 lo = lds_read_tr16(src);
+          const i16x4 hi = lds_read_tr16(src + 8 * kPRow);
+          const i16x8 v8 = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          acc[mb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, v8), pf[j], acc[mb]);
+        }
+        if (mb & 1) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+
+  if constexpr (kFp8) {
+    Fp8Stage st;
+    st.load(p.kv, seq_start, len, 0, tid);
+    st.store(lds, tid);
+    __syncthreads();
+    for (int kt = 0; kt < n_tiles; ++kt) {
+      const bool more = kt + 1 < n_tiles;
+      if (more) st.load(p.kv, seq_start, len, (kt + 1) * kTile, tid);
+      compute(lds + (kt & 1) * kTileElems, kt);
+      if (more) st.store(lds + ((kt + 1) & 1) * kTileElems, tid);
+      __syncthreads();
+    }
+  } else {
+    // tile kt lives in slot kt % 3; tile kt + 2 is copied in while tile kt computes
+    const uint32_t base = lds_addr(lds);
+    const uint8_t* seq_kv = p.kv + (size_t)seq_start * kRowBytes;
+    dma_tile(seq_kv, len, 0, base, wave, lane);
+    if (n_tiles > 1) dma_tile(seq_kv, len, kTile, base + kSlotBytes, wave, lane);
+    for (int kt = 0; kt < n_tiles; ++kt) {
+      if (kt + 1 < n_tiles)
+        wait_vmcnt<kDmaPerWave>();  // this wave's copies of tile kt have landed
+      else
+        wait_vmcnt<0>();
+      __syncthreads();  // everyone's copies of tile kt landed; tile kt - 1 is no longer read
+      if (kt + 2 < n_tiles)
+        dma_tile(seq_kv, len, (kt + 2) * kTile, base + ((kt + 2) % kRing) * kSlotBytes, wave,
+                 lane);
+      compute(lds + (kt % kRing) * (kSlotBytes / 2), kt);
+    }
+  }
+
+  // ---- finalize this lane's row
+  const float l_row = l_run + __shfl_xor(l_run, 32);
+  if (!row_ok) return;
+  const float inv = (l_row > 0.f) ? p.out_scale / l_row : 0.f;
+  const size_t orow = (size_t)seq_start * p.H + r;
+  if (p.lse && g == 0)
+    p.lse[orow] = (l_row > 0.f) ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
+  // acc[mb][i]: dim 32 mb + 8 (i / 4) + 4 g + i % 4
+#pragma unroll
+  for (int mb = 0; mb < 16; ++mb) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int d = 32 * mb + 8 * q4 + 4 * g;
+      const f32x4 v = {acc[mb][4 * q4] * inv, acc[mb][4 * q4 + 1] * inv,
+                       acc[mb][4 * q4 + 2] * inv, acc[mb][4 * q4 + 3] * inv};
+      if (p.out_bf16) {
+        const bf16x4 o = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+        *(bf16x4*)((uint16_t*)p.out + orow * kDV + d) = o;
+      } else {
+        *(f32x4*)((float*)p.out + orow * kDV + d) = v;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const PrefillParams& p, bool kv_fp8, hipStream_t stream) {
+  // upper bound on row blocks over all sequences; surplus work-groups exit at once
+  const long blocks = ((long)p.T * p.H + kRowsPerWg - 1) / kRowsPerWg + p.B;
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  if (kv_fp8)
+    hipLaunchKernelGGL(prefill_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(prefill_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla_impl

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["mla_decode", "mla_verify", "mla_prefill", "mla_merge_lse",
+    for n in ["mla_decode", "mla_verify", "mla_verify_partials", "mla_prefill", "mla_merge_lse",
               "mla_decode_workspace_size", "mla_decode_num_splits", "mla_status_string",
               "mla_version"]:
         assert n in names

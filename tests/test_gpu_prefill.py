@@ -1,0 +1,123 @@
+"""GPU parity of causal prefill against the FP64 oracle, through the C-ABI.
+
+Small packed batches (every row checked) cover ragged sequence lengths around the
+32-token key tile and the 128-row work-group block, an empty sequence, 1 / 5 / 8 / 12 /
+16 heads, BF16 and FP8 latent rows, FP32 and BF16 outputs.  The full-size workload
+(one 32,768-token sequence, 12 heads, BF16 output) runs in the bench's launch
+configuration and is checked on sampled tokens.  Invariants: prefill row i equals
+decode on the prefix of length i + 1, future keys do not matter, runs are bitwise
+repeatable.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as mi
+import oracle
+from parity import bf16_tensor, check_lse, check_out, i32
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+SIGMA = mi.softmax_scale_for()
+
+
+@pytest.fixture(scope="module")
+def mla():
+    import mla_latent_kv_attention_amd as m
+    m.library()
+    assert torch.cuda.is_available()
+    return m
+
+
+def kv_tensor(kv, kv_dtype):
+    if kv_dtype == "bf16":
+        return bf16_tensor(kv, DEV)
+    return torch.from_numpy(np.ascontiguousarray(kv)).to(DEV)
+
+
+def run_gpu(mla, d, kv_dtype, out_dtype=torch.float32, max_seqlen=None):
+    out, lse = mla.prefill(bf16_tensor(d["q"], DEV), kv_tensor(d["kv"], kv_dtype),
+                           i32(d["cu_seqlens"], DEV), softmax_scale=SIGMA,
+                           kv_scale=d["kv_scale"], out_dtype=out_dtype, max_seqlen=max_seqlen)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def run_oracle(d, kv_dtype, tokens=None):
+    return oracle.prefill(d["q"], d["kv"], kv_dtype == "fp8", d["kv_scale"], d["cu_seqlens"],
+                          SIGMA, tokens=tokens)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("H", [12, 8, 16, 1, 5])
+def test_small_parity(mla, kv_dtype, H):
+    lens = [1, 31, 32, 33, 0, 100, 257]
+    d = mi.prefill_inputs(mi.PrefillWorkload("small", lens, H, kv_dtype, seed=3000 + H))
+    print("case", kv_dtype, H, flush=True)
+    out, lse = run_gpu(mla, d, kv_dtype)
+    ref_o, ref_l = run_oracle(d, kv_dtype)
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+
+
+def test_bf16_output_and_single_key_rows(mla):
+    lens = [300, 77]
+    d = mi.prefill_inputs(mi.PrefillWorkload("small", lens, 12, "bf16", seed=3101))
+    out, lse = run_gpu(mla, d, "bf16", out_dtype=torch.bfloat16)
+    ref_o, ref_l = run_oracle(d, "bf16")
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+    # the first token of each sequence sees one key: its output is that row's value part
+    for start in d["cu_seqlens"][:-1]:
+        v = torch.from_numpy(d["kv"][start, :512].view(np.int16)).view(torch.bfloat16)
+        assert torch.equal(out[start].cpu(), v.expand(12, 512))
+
+
+def test_prefill_row_equals_decode_on_prefix(mla):
+    T, H = 512, 12  # one contiguous 512-token block for the decode side
+    d = mi.prefill_inputs(mi.PrefillWorkload("small", [T], H, "bf16", seed=3102))
+    out, lse = run_gpu(mla, d, "bf16")
+    kv = bf16_tensor(d["kv"], DEV).reshape(1, T, 576)
+    for i in [0, 1, 63, 64, 127, 255, 511]:
+        q = bf16_tensor(d["q"][i], DEV).reshape(1, H, 576)
+        o, l = mla.decode(q, kv, torch.zeros((1, 1), dtype=torch.int32, device=DEV),
+                          torch.tensor([i + 1], dtype=torch.int32, device=DEV),
+                          softmax_scale=SIGMA, max_kv_len=i + 1)
+        assert (o[0] - out[i]).abs().max().item() < 2e-3
+        assert (l[0] - lse[i]).abs().max().item() < 2e-5
+
+
+def test_future_keys_do_not_matter_and_runs_repeat(mla):
+    T, H = 400, 12
+    d = mi.prefill_inputs(mi.PrefillWorkload("small", [T], H, "bf16", seed=3103))
+    a, la = run_gpu(mla, d, "bf16")
+    a2, la2 = run_gpu(mla, d, "bf16")
+    assert torch.equal(a, a2) and torch.equal(la, la2)
+    d2 = dict(d)
+    d2["kv"] = d["kv"].copy()
+    d2["kv"][150:] ^= 0x1234
+    b, lb = run_gpu(mla, d2, "bf16")
+    assert torch.equal(a[:150], b[:150]) and torch.equal(la[:150], lb[:150])
+
+
+def test_max_seqlen_hint_does_not_limit_the_work(mla):
+    d = mi.prefill_inputs(mi.PrefillWorkload("small", [200, 90], 12, "fp8", seed=3104))
+    out, lse = run_gpu(mla, d, "fp8", max_seqlen=8)
+    ref_o, ref_l = run_oracle(d, "fp8")
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+
+
+def test_full_prefill_t32768_h12_bf16(mla):
+    w = mi.WORKLOADS["prefill_t32768_h12_bf16"]
+    d = mi.prefill_inputs(w)
+    print("full", w.name, flush=True)
+    out, lse = run_gpu(mla, d, "bf16", out_dtype=torch.bfloat16, max_seqlen=32768)
+    rng = np.random.default_rng(17)
+    toks = np.unique(np.concatenate([[0, 1, 31, 32, 127, 32767],
+                                     rng.choice(32768, 14, replace=False)])).astype(np.int64)
+    ref_o, ref_l = run_oracle(d, "bf16", tokens=toks)
+    idx = torch.from_numpy(toks).to(DEV)
+    check_out(out[idx], ref_o)
+    check_lse(lse[idx], ref_l)

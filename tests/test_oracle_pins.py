@@ -410,3 +410,19 @@ def test_latent_cache_bytes_match_pages():
     share = g["kv_bytes_142000_tokens_dcp8_share"]
     assert total["value"] // share["shards"] == share["value"]
     assert round(share["value"] / 1e6) == 245
+
+
+def test_accounting_matches_pages_and_closed_forms():
+    from mla_latent_kv_attention_amd import accounting as acc
+    g = json.load(open(os.path.join(GOLDEN, "pages_closed_forms.json")))
+    total = g["kv_bytes_142000_tokens_all_layers"]
+    assert acc.row_bytes("fp8") == g["latent_row_bytes_fp8"]["value"]
+    per_layer = acc.decode_bytes([total["tokens"]], 1, 1, "fp8", block_size=64)
+    kv_only = total["tokens"] * acc.row_bytes("fp8")
+    assert kv_only * g["mla_layers_kimi_k3"]["value"] == total["value"]
+    assert per_layer == kv_only + 4 * (-(-total["tokens"] // 64)) + (576 * 2 + 512 * 4 + 4)
+    # causal triangle: 12 heads x T(T+1)/2 x 2,176 at T = 32,768
+    assert acc.prefill_flops([32768], 12) == 12 * 536887296 * 2176 == 14019201073152
+    # decode flops: each query row sees exactly its visible keys
+    assert acc.decode_flops([10, 7], 4, 2) == 2 * 2176 * ((7 + 8 + 9 + 10) + (4 + 5 + 6 + 7))
+    assert acc.decode_flops([100], 1, 12, kv_begin=[30], kv_end=[60]) == 12 * 30 * 2176
