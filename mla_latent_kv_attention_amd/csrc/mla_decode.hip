@@ -14,11 +14,13 @@
 // query rows sit in LDS, read by all four).  Per step:
 //   1. every lane loads 8 (bf16) or 16 (fp8) key values of one token straight
 //      from the paged cache into MFMA A-operand registers (16 B per load;
-//      fp8 is widened to bf16 exactly);
-//   2. S^T[16 tokens x 16 rows] = K Q^T with 18 bf16 MFMA 16x16x32 (Q^T,
-//      the B operand, comes from LDS);
+//      fp8 is widened to bf16 exactly); a ring of register buffers keeps the
+//      next 2 (fp8) or 1 (bf16) steps in flight;
+//   2. S^T[16 tokens x 16 rows] = K Q^T with 18 bf16 MFMA 16x16x32 (Q^T, the
+//      B operand, is read from LDS three k-steps ahead of its MFMA);
 //   3. masking and the online softmax run on the 4 scores each lane holds,
-//      with cross-lane max / sum over the 4 lane groups of a row; the running
+//      with cross-lane max / sum over the 4 lane groups of a row through the
+//      VALU lane swaps (v_permlane16/32_swap, no LDS round trip); the running
 //      max is only moved (and the accumulator rescaled) when it trails the
 //      chunk max by more than 2^8, which keeps the rescale off the hot path;
 //   4. the value part (first 512 dims) of the same registers goes to a per-wave
@@ -71,7 +73,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodePara
   constexpr int kLoads = kFp8 ? 9 : 18;  // 16-byte loads per lane per step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;  // token (A rows) / query row (B, C columns)
   const int grp = lane >> 4;  // k-group (A, B) / 4-row group (C)
 
@@ -96,8 +98,10 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodePara
   const bool row_ok = r < p.R;
   const int hi_row = row_ok ? min(hi_all, L - p.P + r / p.H + 1) : lo;
 
-  // The row block's queries go to LDS once (rows past R are zero); the B
-  // operand Q^T is read from there each step, shared by the four waves.
+  // The row block's queries go to LDS once (rows past R are zero); every step
+  // reads its Q^T fragments (B operand of the score MFMA) from there, three
+  // k-steps ahead of their MFMA, which keeps the 16 query rows out of the
+  // register budget.
   for (int i = tid; i < 16 * (kDK / 8); i += 256) {
     const int row = i / (kDK / 8), c8 = i % (kDK / 8);
     const int rq = rb * 16 + row;
@@ -107,6 +111,7 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodePara
   }
   __syncthreads();
   const uint16_t* qsrc = sm.q + col * kDK;
+  auto qfrag = [&](int kk) { return *(const bf16x8*)(qsrc + kdim<kFp8>(kk, grp)); };
 
   f32x4 acc[32];
 #pragma unroll
@@ -128,26 +133,44 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodePara
   };
 
   auto process_step = [&](const u32x4* raw, int t0) {
-    bf16x8 kf[kKSteps];
+    // scores: lane (col, grp) gets tokens t0 + 4 * grp + i of query row `col`; the value
+    // part of each fragment goes to this wave's LDS tile on the way (bf16, token-major).
+    // Schedule: the Q^T fragments of three k-steps are read before the first MFMA,
+    // then every MFMA is followed by the read of the fragment three steps later.
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+    uint16_t* vrow = vt + col * kVRow;
     if constexpr (kFp8) {
 #pragma unroll
-      for (int j = 0; j < 9; ++j) fp8x16_to_bf16(raw[j], kf[2 * j], kf[2 * j + 1]);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        *(bf16x8*)(vt + col * kVRow + 64 * j + 16 * grp) = kf[2 * j];
-        *(bf16x8*)(vt + col * kVRow + 64 * j + 16 * grp + 8) = kf[2 * j + 1];
+      for (int j = 0; j < 9; ++j) {
+        bf16x8 ka, kb;
+        fp8x16_to_bf16(raw[j], ka, kb);
+        if (j < 8) {
+          *(bf16x8*)(vrow + 64 * j + 16 * grp) = ka;
+          *(bf16x8*)(vrow + 64 * j + 16 * grp + 8) = kb;
+        }
+        sc = mfma_16x16x32(ka, qfrag(2 * j), sc);
+        sc = mfma_16x16x32(kb, qfrag(2 * j + 1), sc);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) kf[kk] = __builtin_bit_cast(bf16x8, raw[kk]);
-#pragma unroll
-      for (int kk = 0; kk < 16; ++kk) *(bf16x8*)(vt + col * kVRow + 32 * kk + 8 * grp) = kf[kk];
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        const bf16x8 k = __builtin_bit_cast(bf16x8, raw[kk]);
+        if (kk < 16) *(bf16x8*)(vrow + 32 * kk + 8 * grp) = k;
+        sc = mfma_16x16x32(k, qfrag(kk), sc);
+      }
     }
-    // scores: lane (col, grp) gets tokens t0 + 4 * grp + i of query row `col`
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+
+    {
+      constexpr int kDsRead = 0x100, kMfma = 0x8, kAhead = 3;
+      __builtin_amdgcn_sched_group_barrier(kDsRead, kAhead, 0);
 #pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk)
-      sc = mfma_16x16x32(kf[kk], *(const bf16x8*)(qsrc + kdim<kFp8>(kk, grp)), sc);
+      for (int i = 0; i < kKSteps - kAhead; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kMfma, kAhead, 0);
+    }
 
     float sv[4];
     float cm = -INFINITY;
@@ -181,21 +204,44 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodePara
     wave_lds_fence();
     const uint16_t* vsrc = vt + (4 * grp + (col >> 2)) * kVRow + 4 * (col & 3);
 #pragma unroll
-    for (int m = 0; m < 32; ++m) acc[m] = mfma_16x16x16(lds_read_tr16(vsrc + 16 * m), pf, acc[m]);
+    for (int m = 0; m < 32; ++m) {
+      acc[m] = mfma_16x16x16(lds_read_tr16(vsrc + 16 * m), pf, acc[m]);
+    }
     wave_lds_fence();
   };
 
-  // the next step's loads are in flight while the current step computes
-  u32x4 cur[kLoads], nxt[kLoads];
+  // A ring of kDepth register buffers per wave: the loads of the next kDepth - 1
+  // steps are in flight while a step computes (one step moves 9 KB of fp8 or
+  // 18 KB of bf16 rows per wave).  The loop is unrolled by kDepth so every buffer
+  // index is a compile-time constant.
+  constexpr int kDepth = kFp8 ? 3 : 2;
   constexpr int kStride = kStep * kWaves;
-  int t0 = t_begin + kStep * wave;
-  if (t0 < t_end) load_step(t0, cur);
-  for (; t0 < t_end; t0 += kStride) {
-    if (t0 + kStride < t_end) load_step(t0 + kStride, nxt);
-    process_step(cur, t0);
+  const int t_first = t_begin + kStep * wave;
+  const int n_steps = t_first < t_end ? (t_end - t_first + kStride - 1) / kStride : 0;
+  // Every step issues the same loads (prefetches past the wave's last step re-read
+  // that step), and the steady-state loop below has no branch around them, so the
+  // compiler counts them exactly and keeps the whole ring in flight.
+  u32x4 ring[kDepth][kLoads];
+  const int last_t0 = t_first + (n_steps - 1) * kStride;
+  if (n_steps > 0) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) cur[i] = nxt[i];
+    for (int u = 0; u < kDepth - 1; ++u) load_step(min(t_first + u * kStride, last_t0), ring[u]);
   }
+  int i0 = 0;
+  for (; i0 + kDepth <= n_steps; i0 += kDepth) {
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const int i = i0 + u;
+      load_step(min(t_first + (i + kDepth - 1) * kStride, last_t0),
+                ring[(u + kDepth - 1) % kDepth]);
+      __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the step computes
+      process_step(ring[u], t_first + i * kStride);
+    }
+  }
+  // tail: fewer than kDepth steps remain and all of them are already loaded
+#pragma unroll
+  for (int u = 0; u < kDepth - 1; ++u)
+    if (i0 + u < n_steps) process_step(ring[u], t_first + (i0 + u) * kStride);
 
   // ---- merge the four waves ----
   const float l_row = wave_sum16x4(l_run);
@@ -268,7 +314,10 @@ __global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodePara
   }
 }
 
-// One work-group of 128 threads per row; each thread owns 4 of the 512 dims.
+// One work-group of 128 threads per row; each thread owns 4 of the 512 dims.  The
+// partial rows are loaded unconditionally (a split without keys for the row left
+// its slot unwritten; its weight selects the value away), so the loads of several
+// splits are in flight together.
 __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_out,
                                                     const float* __restrict__ part_lse, int S,
                                                     int N, void* out, int out_bf16, float* lse) {
@@ -279,12 +328,13 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   if (M != -INFINITY) {
+#pragma unroll 8
     for (int s = 0; s < S; ++s) {
       const float x = part_lse[(size_t)s * N + n];
-      if (x == -INFINITY) continue;
-      const float w = expf(x - M);
+      const float w = (x == -INFINITY) ? 0.f : expf(x - M);
+      const f32x4 v = *(const f32x4*)(part_out + ((size_t)s * N + n) * kDV + d);
       L += w;
-      acc += w * *(const f32x4*)(part_out + ((size_t)s * N + n) * kDV + d);
+      if (w > 0.f) acc += w * v;
     }
     acc *= 1.f / L;
   }

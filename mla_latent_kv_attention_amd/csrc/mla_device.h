@@ -61,20 +61,72 @@ __device__ __forceinline__ void fp8x16_to_bf16(u32x4 w, bf16x8& a, bf16x8& b) {
   b = (bf16x8){p4.x, p4.y, p5.x, p5.y, p6.x, p6.y, p7.x, p7.y};
 }
 
+// x *= s for MFMA accumulator values kept in AGPRs: each element is read into a
+// VGPR, scaled and written back, so the accumulator keeps its register class
+// across a loop (a plain VALU multiply on it makes the compiler carry every
+// accumulator value through VGPRs on every iteration).
+template <int kN>
+__device__ __forceinline__ void scale_agpr(float __attribute__((ext_vector_type(kN)))& acc,
+                                           float s) {
+#pragma unroll
+  for (int i = 0; i < kN; ++i) {
+    float x = acc[i];
+    float t;
+    asm volatile(
+        "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1"
+        : "+a"(x), "=&v"(t)
+        : "v"(s));
+    acc[i] = x;
+  }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// Lane pairs {l, l ^ 32} and {l, l ^ 16} through the gfx950 VALU lane swaps
+// (no LDS round trip).  permlane32_swap(a, b) exchanges lanes 32-63 of a with
+// lanes 0-31 of b; with a = b = v the two results hold v[l & 31] and
+// v[(l & 31) + 32].  permlane16_swap does the same for odd / even 16-lane rows.
+__device__ __forceinline__ void xor32_pair(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void xor16_pair(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ float wave_max16x4(float v) {
   // max over lanes {l, l ^ 16, l ^ 32, l ^ 48}
-  v = fmaxf(v, __shfl_xor(v, 16));
-  v = fmaxf(v, __shfl_xor(v, 32));
-  return v;
+  float a, b;
+  xor16_pair(v, a, b);
+  v = fmaxf(a, b);
+  xor32_pair(v, a, b);
+  return fmaxf(a, b);
 }
 
 __device__ __forceinline__ float wave_sum16x4(float v) {
-  v += __shfl_xor(v, 16);
-  v += __shfl_xor(v, 32);
-  return v;
+  float a, b;
+  xor16_pair(v, a, b);
+  v = a + b;
+  xor32_pair(v, a, b);
+  return a + b;
+}
+
+__device__ __forceinline__ float wave_max_xor32(float v) {
+  float a, b;
+  xor32_pair(v, a, b);
+  return fmaxf(a, b);
+}
+
+__device__ __forceinline__ float wave_sum_xor32(float v) {
+  float a, b;
+  xor32_pair(v, a, b);
+  return a + b;
 }
 
 // Keep the compiler from moving LDS accesses across this point; lanes of one

@@ -96,6 +96,21 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Scheduling pattern for a chain of kMfma MFMAs, each fed by kReads LDS reads:
+// the reads for the first kAhead MFMAs go first, then each MFMA is followed by
+// the reads of the MFMA kAhead places later.
+template <int kMfma, int kReads, int kAhead>
+__device__ __forceinline__ void sched_pipeline() {
+  constexpr int kDsRead = 0x100, kMfmaMask = 0x8;
+  __builtin_amdgcn_sched_group_barrier(kDsRead, kReads * kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < kMfma - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfmaMask, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, kReads, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfmaMask, kAhead, 0);
+}
+
 // FP8 tiles go through registers: 16 codes per 16-byte load, widened exactly to
 // bf16 on the way into the same padded LDS layout.
 struct Fp8Stage {
@@ -210,15 +225,14 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   // live range and cost far more than the few skipped diagonal tiles.
   auto compute = [&](const uint16_t* buf, int kt) {
     {
-      // groups of 6 k-steps: bounds how many K fragments the scheduler keeps in flight
+      // K fragments are read two k-steps ahead of the MFMA that consumes them; the
+      // group barriers pin that interleave (left alone, the scheduler waits on each
+      // read right before its MFMA)
       f32x16 sc = {};
 #pragma unroll
-      for (int k6 = 0; k6 < kKSteps; k6 += 6) {
-#pragma unroll
-        for (int kk = k6; kk < k6 + 6; ++kk)
-          sc = mfma_32x32x16(*(const bf16x8*)(buf + a_off + 16 * kk), qf[kk], sc);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int kk = 0; kk < kKSteps; ++kk)
+        sc = mfma_32x32x16(*(const bf16x8*)(buf + a_off + 16 * kk), qf[kk], sc);
+      sched_pipeline<kKSteps, 1, 2>();
       // lane (n, g) holds tokens kt*32 + 8 (i/4) + 4 g + i%4 of row n
       float sv[16];
       float cm = -INFINITY;
@@ -263,8 +277,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
           const i16x8 v8 = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
           acc[mb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, v8), pf[j], acc[mb]);
         }
-        if (mb & 1) __builtin_amdgcn_sched_barrier(0);
       }
+      sched_pipeline<32, 2, 2>();
     }
   };
 

@@ -79,13 +79,21 @@ def test_prefill_row_equals_decode_on_prefix(mla):
     d = mi.prefill_inputs(mi.PrefillWorkload("small", [T], H, "bf16", seed=3102))
     out, lse = run_gpu(mla, d, "bf16")
     kv = bf16_tensor(d["kv"], DEV).reshape(1, T, 576)
-    for i in [0, 1, 63, 64, 127, 255, 511]:
+    toks = [0, 1, 63, 64, 127, 255, 511]
+    ref_o, ref_l = run_oracle(d, "bf16", tokens=np.array(toks, np.int64))
+    for k, i in enumerate(toks):
         q = bf16_tensor(d["q"][i], DEV).reshape(1, H, 576)
         o, l = mla.decode(q, kv, torch.zeros((1, 1), dtype=torch.int32, device=DEV),
                           torch.tensor([i + 1], dtype=torch.int32, device=DEV),
                           softmax_scale=SIGMA, max_kv_len=i + 1)
-        assert (o[0] - out[i]).abs().max().item() < 2e-3
-        assert (l[0] - lse[i]).abs().max().item() < 2e-5
+        torch.cuda.synchronize()
+        # both paths meet the parity bar; they round P against different running maxima,
+        # so they agree with each other to the same bar, not bitwise
+        check_out(o[0], ref_o[k], "decode on prefix %d" % i)
+        check_out(out[i], ref_o[k], "prefill row %d" % i)
+        check_lse(l[0], ref_l[k])
+        check_lse(lse[i], ref_l[k])
+        assert (o[0] - out[i]).abs().max().item() <= 1e-2
 
 
 def test_future_keys_do_not_matter_and_runs_repeat(mla):
