@@ -4,8 +4,9 @@
 A step is one pass of the decode hot path over one batch of the headline workload:
 32 sequences, 12 heads, one query each, per-sequence contexts uniform in [4096, 16384],
 FP8 E4M3 latent rows with a per-tensor scale in 64-token pages behind a shuffled block
-table (synthetic, seeded).  One step = the split-KV partial kernel + the LSE merge, both
-through the C-ABI; the inputs are resident in HBM before timing starts.  KV pools rotate
+table (synthetic, seeded).  One step = one mla_verify call through the C-ABI: a single
+persistent kernel that streams the batch's latent rows and merges split sequences in the
+same launch; the inputs are resident in HBM before timing starts.  KV pools rotate
 over several copies so the 256 MB last-level cache cannot hold the one being read.
 
 Printed: ONE JSON line (metric, value = algorithmic KV-read GB/s of the whole step,
@@ -57,7 +58,7 @@ def traffic_from_profile(kernel_file: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(q, cache, alg_bytes, min_seconds=10.0, max_reps=20):
+def cpu_baseline(q, cache, alg_bytes, min_seconds=10.0, max_reps=400):
     """The FP64 oracle on the whole batch (every row), repeated until >= min_seconds."""
     import oracle
     import mla_inputs as mi
@@ -82,7 +83,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--rotate", type=int, default=3, help="KV pool copies cycled over")
-    ap.add_argument("--num-splits", type=int, default=0, help="0 = automatic split plan")
+    ap.add_argument("--num-splits", type=int, default=0, help="pieces; 0 = automatic plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=5)
@@ -116,22 +117,20 @@ def main():
     kv0, bt, sl = cache_to_device(cache, dev)
     pools = [kv0] + [kv0.clone() for _ in range(max(0, args.rotate - 1))]
     q = bf16_tensor(q_np, dev).reshape(B, P, H, 576)
-    S = mla.decode_num_splits(B, P, H, max_len, args.num_splits)
+    W = mla.decode_num_splits(B, P, H, max_len, args.num_splits)
     N = B * P * H
-    part_out = torch.empty((S, N, 512), dtype=torch.float32, device=dev)
-    part_lse = torch.empty((S, N), dtype=torch.float32, device=dev)
-    out = torch.empty((N, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    out = torch.empty((B, P, H, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, P, H), dtype=torch.float32, device=dev)
+    # one zero-filled workspace for every call: each call leaves its counters zero
+    workspace = torch.zeros(max(1, mla.decode_workspace_size(B, P, H, max_len, args.num_splits)),
+                            dtype=torch.uint8, device=dev)
     sigma = w.softmax_scale
+    launches = [mla.verify_launcher(q, kv, bt, sl, softmax_scale=sigma, kv_scale=cache.kv_scale,
+                                    max_kv_len=max_len, out=out, lse=lse, workspace=workspace,
+                                    num_splits=args.num_splits) for kv in pools]
 
     def step(i):
-        kv = pools[i % len(pools)]
-        mla.verify_partials(q, kv, bt, sl, softmax_scale=sigma, kv_scale=cache.kv_scale,
-                            max_kv_len=max_len, num_splits=args.num_splits, part_out=part_out,
-                            part_lse=part_lse)
-
-    def merge():
-        mla.merge_lse(part_out, part_lse, out=out, lse=lse)
+        launches[i % len(launches)]()
 
     # parity on the timed buffers (every pool) before timing
     import oracle
@@ -141,40 +140,35 @@ def main():
     idx = torch.from_numpy(rows).to(dev)
     for i in range(len(pools)):
         step(i)
-        merge()
         torch.cuda.synchronize()
-        check_out(out[idx], ref_o, "decode out (pool %d)" % i)
-        check_lse(lse[idx], ref_l, "decode lse (pool %d)" % i)
-    log("parity ok on %d sampled rows, %d pools, %d splits" % (len(rows), len(pools), S))
+        check_out(out.reshape(N, 512)[idx], ref_o, "decode out (pool %d)" % i)
+        check_lse(lse.reshape(N)[idx], ref_l, "decode lse (pool %d)" % i)
+    log("parity ok on %d sampled rows, %d pools, %d pieces" % (len(rows), len(pools), W))
 
     alg_bytes = acc.decode_bytes(L, P, H, "fp8", out_bytes=4, block_size=cache.block_size)
     alg_flops = acc.decode_flops(L, P, H)
 
     for i in range(args.warmup):
         step(i)
-        merge()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        e0, e1, e2 = ev[i]
-        e0.record(stream)
+        e0, e1 = ev[i]
+        e0.record(stream)  # the library launches on torch's current stream
         step(args.warmup + i)
         e1.record(stream)
-        merge()
-        e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    part_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
-    merge_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    kern_ms = np.array([a.elapsed_time(b) for a, b in ev])
     ms_per_step = wall * 1e3 / args.steps
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = alg_bytes / (part_ms.mean() * 1e-3) / 1e9
+    achieved = alg_bytes / (kern_ms.mean() * 1e-3) / 1e9
     traffic = traffic_from_profile("mla_decode.hip", DECODE_WORKLOAD)
-    log("decode: %.1f us/step wall, partial kernel %.1f us (p10 %.1f, p90 %.1f), merge %.1f us"
-        % (ms_per_step * 1e3, part_ms.mean() * 1e3, np.percentile(part_ms, 10) * 1e3,
-           np.percentile(part_ms, 90) * 1e3, merge_ms.mean() * 1e3))
+    log("decode: %.1f us/step wall, kernel %.1f us (p10 %.1f, p90 %.1f)"
+        % (ms_per_step * 1e3, kern_ms.mean() * 1e3, np.percentile(kern_ms, 10) * 1e3,
+           np.percentile(kern_ms, 90) * 1e3))
 
     result = {
         "metric": METRIC,
@@ -191,14 +185,13 @@ def main():
         "data": "synthetic (seeded N(0,1), FP8 E4M3 per-tensor scale, shuffled 64-token pages)",
         "config": {"workload": DECODE_WORKLOAD, "batch": B, "heads": H, "query_positions": P,
                    "context": "uniform [4096, 16384]", "total_keys": int(sum(L)),
-                   "kv_dtype": "fp8_e4m3", "block_size": cache.block_size, "splits": S,
+                   "kv_dtype": "fp8_e4m3", "block_size": cache.block_size, "pieces": W,
                    "kv_pool_copies": len(pools), "algorithmic_bytes": alg_bytes,
                    "algorithmic_flops": alg_flops},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_partial_kernel<fp8>",
-                     "kernel_us": round(float(part_ms.mean()) * 1e3, 2),
-                     "merge_us": round(float(merge_ms.mean()) * 1e3, 2)},
+                     "traffic": traffic, "kernel": "decode_kernel<fp8>",
+                     "kernel_us": round(float(kern_ms.mean()) * 1e3, 2)},
     }
 
     # ---------------- prefill (the metric's second half) ----------------

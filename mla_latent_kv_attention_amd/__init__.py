@@ -9,7 +9,6 @@ raise instead of computing anything.
 Entry points (same names as the C-ABI):
   decode(q, kv_cache, block_table, seq_lens, ...)   one query position per sequence
   verify(q, kv_cache, block_table, seq_lens, ...)   P query positions, causal among them
-  verify_partials(...)                              verify's split stage without the merge
   prefill(q, kv, cu_seqlens, ...)                   causal attention of packed sequences
   merge_lse(part_out, part_lse, ...)                merge partials by log-sum-exp
 """
@@ -57,8 +56,6 @@ def library() -> ctypes.CDLL:
         P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.mla_verify.restype = I
         lib.mla_verify.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, I, F, P, I, P, I, P, Z, P]
-        lib.mla_verify_partials.restype = I
-        lib.mla_verify_partials.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, I, F, I, P, P, P]
         lib.mla_decode.restype = I
         lib.mla_decode.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, F, P, I, P, I, P, Z, P]
         lib.mla_prefill.restype = I
@@ -116,12 +113,27 @@ def _dev_i32(t: Optional[torch.Tensor], name: str, dev: torch.device):
 
 def decode_num_splits(B: int, P: int, H: int, max_kv_len: int, num_splits: int = 0,
                       num_cus: int = 0) -> int:
-    """Splits per sequence the call would use (num_cus = 0: the current device)."""
+    """Pieces the batch's key steps are divided into (num_cus = 0: the current device)."""
     return library().mla_decode_num_splits(B, P, H, max_kv_len, num_splits, num_cus)
 
 
 def decode_workspace_size(B: int, P: int, H: int, max_kv_len: int, num_splits: int = 0) -> int:
     return library().mla_decode_workspace_size(B, P, H, max_kv_len, num_splits)
+
+
+# Zero-filled decode workspaces, one per (device, stream): every call leaves the
+# workspace's counters zero, so calls ordered on one stream can share it.
+_workspaces = {}
+
+
+def decode_workspace(nbytes: int, dev: torch.device) -> torch.Tensor:
+    """A zero-filled workspace of at least nbytes for calls on dev's current stream."""
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=dev)
+        _workspaces[key] = ws
+    return ws
 
 
 def verify(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
@@ -136,7 +148,9 @@ def verify(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
     Query j of sequence b is position seq_lens[b] - P + j and sees keys
     kv_begin <= t < min(kv_end, seq_lens[b] - P + j + 1).  Returns (out [B, P, H, 512],
     lse [B, P, H] fp32 or None).  ``max_kv_len`` (host int) bounds any sequence's key
-    range; when omitted it is read back from the device (a synchronisation).
+    range; when omitted it is read back from the device (a synchronisation).  A
+    caller-supplied ``workspace`` (uint8) must be zero-filled before its first use; the
+    calls keep it that way.
     """
     lib = library()
     if q.dim() != 4 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16:
@@ -163,7 +177,7 @@ def verify(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
         lse = torch.empty((B, P, H), dtype=torch.float32, device=dev)
     ws_need = lib.mla_decode_workspace_size(B, P, H, max_kv_len, num_splits)
     if workspace is None and ws_need > 0:
-        workspace = torch.empty(ws_need, dtype=torch.uint8, device=dev)
+        workspace = decode_workspace(ws_need, dev)
     st = lib.mla_verify(
         _ptr(q), _ptr(kv_cache), kvd, float(kv_scale), _ptr(block_table),
         block_table.shape[1], kv_cache.shape[1], _ptr(seq_lens), _ptr(kv_begin), _ptr(kv_end),
@@ -174,39 +188,40 @@ def verify(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
     return out, lse
 
 
-def verify_partials(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+def verify_launcher(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                     seq_lens: torch.Tensor, *, softmax_scale: float, kv_scale: float = 1.0,
-                    kv_begin: Optional[torch.Tensor] = None, kv_end: Optional[torch.Tensor] = None,
-                    max_kv_len: int, num_splits: int = 0,
-                    part_out: Optional[torch.Tensor] = None,
-                    part_lse: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
-    """The split stage of verify alone: per-split (normalised out [S, B*P*H, 512], lse [S, B*P*H]).
-
-    merge_lse(part_out, part_lse) gives verify's result for the same arguments.
-    """
+                    max_kv_len: int, out: torch.Tensor, lse: Optional[torch.Tensor],
+                    workspace: Optional[torch.Tensor], num_splits: int = 0,
+                    kv_begin: Optional[torch.Tensor] = None,
+                    kv_end: Optional[torch.Tensor] = None):
+    """verify's C call with every argument marshalled once: returns a function of no
+    arguments that launches it on the stream current at preparation time.  For loops that
+    launch the same call many times (the tensors must stay alive and keep their storage)."""
     lib = library()
-    if q.dim() != 4 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16:
-        raise TypeError("q must be [B, P, H, 576] bfloat16")
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16 or \
+            not q.is_contiguous():
+        raise TypeError("q must be a contiguous [B, P, H, 576] bfloat16 tensor")
+    if not kv_cache.is_contiguous() or not out.is_contiguous():
+        raise TypeError("kv_cache and out must be contiguous")
     dev = q.device
     B, P, H, _ = q.shape
-    q = q.contiguous()
-    kv_cache = kv_cache.contiguous()
-    S = lib.mla_decode_num_splits(B, P, H, int(max_kv_len), int(num_splits), 0)
-    if S < 0:
-        raise MlaError("mla_decode_num_splits", S)
-    N = B * P * H
-    if part_out is None:
-        part_out = torch.empty((S, N, HEAD_DIM_V), dtype=torch.float32, device=dev)
-    if part_lse is None:
-        part_lse = torch.empty((S, N), dtype=torch.float32, device=dev)
-    st = lib.mla_verify_partials(
-        _ptr(q), _ptr(kv_cache), _kv_dtype(kv_cache), float(kv_scale),
-        _ptr(_dev_i32(block_table, "block_table", dev)), block_table.shape[1], kv_cache.shape[1],
-        _ptr(_dev_i32(seq_lens, "seq_lens", dev)), _ptr(_dev_i32(kv_begin, "kv_begin", dev)),
-        _ptr(_dev_i32(kv_end, "kv_end", dev)), B, P, H, int(max_kv_len), float(softmax_scale),
-        int(num_splits), _ptr(part_out), _ptr(part_lse), _stream(dev))
-    _check("mla_verify_partials", st)
-    return part_out, part_lse
+    need = lib.mla_decode_workspace_size(B, P, H, int(max_kv_len), int(num_splits))
+    if need > 0 and (workspace is None or workspace.numel() < need):
+        raise MlaError("mla_verify", -3)
+    args = (_ptr(q), _ptr(kv_cache), _kv_dtype(kv_cache), float(kv_scale),
+            _ptr(_dev_i32(block_table, "block_table", dev)), block_table.shape[1],
+            kv_cache.shape[1], _ptr(_dev_i32(seq_lens, "seq_lens", dev)),
+            _ptr(_dev_i32(kv_begin, "kv_begin", dev)), _ptr(_dev_i32(kv_end, "kv_end", dev)),
+            B, P, H, int(max_kv_len), float(softmax_scale), _ptr(out), _out_dtype(out.dtype),
+            _ptr(lse), int(num_splits), _ptr(workspace),
+            0 if workspace is None else workspace.numel(), _stream(dev))
+    fn = lib.mla_verify
+
+    def launch():
+        st = fn(*args)
+        if st != 0:
+            raise MlaError("mla_verify", st)
+    return launch
 
 
 def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,

@@ -1,7 +1,7 @@
 // mla_api.cpp -- the C-ABI entry points declared in include/mla.h.
 //
-// Host work only: argument checks (before any launch), the split-KV planner,
-// the workspace carve-up and the kernel launches on the caller's stream.
+// Host work only: argument checks (before any launch), the piece planner of the
+// persistent decode, the workspace carve-up and the kernel launches on the caller's stream.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -12,7 +12,13 @@
 
 namespace {
 
-constexpr int kStepTokens = 64;       // tokens one work-group consumes per round (4 waves x 16)
+constexpr int kStepTokens = 16;        // tokens per step of the concatenated step list
+constexpr int kMinStepsPerPiece = 8;   // two steps per wave before a piece pays for its merge
+// What a piece pays for each sequence it touches (query load, wave merge, partial
+// publish), in 16-token steps of streaming; measured per cache dtype.
+constexpr int kSegmentStepsFp8 = 30;
+constexpr int kSegmentStepsBf16 = 18;
+constexpr int kMaxPieces = 1 << 16;
 constexpr int kMaxDevices = 64;
 constexpr size_t kAlign = 256;
 
@@ -33,40 +39,42 @@ int current_cu_count() {
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
-  int R, RB, S, chunk;
+  int R, RB, W;
 };
 
-// Split plan.  Work-groups = B * RB * S; aim for a few per CU so long
-// histories spread over the whole chip and short ones still fill it, with every
-// split a whole number of 64-token rounds.  The last split takes any keys past
-// S * chunk, so a wrong max_kv_len hint costs time, never correctness.
+// Piece plan.  The kernel is persistent: W pieces x RB row blocks work-groups,
+// one per CU (a work-group's LDS keeps it alone on its CU), each streaming an
+// equal share of the batch's 16-token steps.  Short batches get fewer pieces
+// so that every piece keeps its four waves busy; the max_kv_len hint only sizes
+// W, and a wrong hint costs time, never correctness.
 Plan make_plan(int B, int P, int H, int max_kv_len, int num_splits, int cus) {
   Plan pl;
   pl.R = P * H;
   pl.RB = (pl.R + 15) / 16;
-  const long len = max_kv_len > 0 ? max_kv_len : 1;
-  const long rounds = (len + kStepTokens - 1) / kStepTokens;
-  long S;
   if (num_splits > 0) {
-    S = num_splits;
-  } else {
-    const int target = 2 * (cus > 0 ? cus : 256);
-    const long units = (long)(B > 0 ? B : 1) * pl.RB;
-    S = (target + units - 1) / units;
-    if (S > rounds) S = rounds;
-    if (S < 1) S = 1;
+    pl.W = num_splits < kMaxPieces ? num_splits : kMaxPieces;
+    return pl;
   }
-  long chunk_rounds = (rounds + S - 1) / S;
-  pl.chunk = (int)(chunk_rounds * kStepTokens);
-  if (num_splits <= 0) S = (rounds + chunk_rounds - 1) / chunk_rounds;
-  pl.S = (int)S;
+  long W = (cus > 0 ? cus : 256) / pl.RB;
+  const long steps = (long)(B > 0 ? B : 1) * (((long)max_kv_len + kStepTokens - 1) / kStepTokens);
+  const long by_steps = (steps + kMinStepsPerPiece - 1) / kMinStepsPerPiece;
+  if (W > by_steps) W = by_steps;
+  if (W < 1) W = 1;
+  pl.W = (int)W;
   return pl;
 }
 
+// Workspace: a fixed block of completion counters at offset 0 (its place and size do
+// not depend on the call's shape, so a workspace that calls of any shape leave zero
+// stays zero there), then the partial rows and lse of the (W + B) slots.  One piece
+// needs none.
+constexpr size_t kCounterBytes = (size_t)MLA_MAX_COUNTERS * sizeof(int);
+
 size_t workspace_bytes_for(const Plan& pl, int B) {
-  if (pl.S <= 1) return 0;
-  const size_t rows = (size_t)pl.S * B * pl.R;
-  return align_up(rows * MLA_HEAD_DIM_V * sizeof(float)) + align_up(rows * sizeof(float));
+  if (pl.W <= 1) return 0;
+  const size_t rows = (size_t)(pl.W + B) * pl.R;
+  return kCounterBytes + align_up(rows * MLA_HEAD_DIM_V * sizeof(float)) +
+         align_up(rows * sizeof(float));
 }
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.f; }
@@ -97,7 +105,7 @@ int mla_decode_num_splits(int B, int P, int H, int max_kv_len, int num_splits, i
     return MLA_E_INVAL;
   if ((long)P * H > MLA_MAX_ROWS) return MLA_E_UNSUPPORTED;
   const int cus = num_cus > 0 ? num_cus : current_cu_count();
-  return make_plan(B, P, H, max_kv_len, num_splits, cus).S;
+  return make_plan(B, P, H, max_kv_len, num_splits, cus).W;
 }
 
 size_t mla_decode_workspace_size(int B, int P, int H, int max_kv_len, int num_splits) {
@@ -108,7 +116,7 @@ size_t mla_decode_workspace_size(int B, int P, int H, int max_kv_len, int num_sp
 
 namespace {
 
-// Shared argument checks and parameter setup of mla_verify / mla_verify_partials.
+// Argument checks and parameter setup of mla_verify.
 mla_status setup_decode(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
                         const int32_t* block_table, int max_blocks_per_seq, int block_size,
                         const int32_t* seq_lens, const int32_t* kv_begin, const int32_t* kv_end,
@@ -121,10 +129,12 @@ mla_status setup_decode(const void* q, const void* kv_cache, int kv_dtype, float
   if (!std::isfinite(softmax_scale)) return MLA_E_INVAL;
   if (kv_dtype == MLA_DTYPE_FP8_E4M3 && !finite_positive(kv_scale)) return MLA_E_INVAL;
   if (B > 0 && (!q || !kv_cache || !block_table || !seq_lens)) return MLA_E_INVAL;
+  // more sequences x row blocks than counters: only the single-piece plan (no workspace)
+  if ((long)B * ((P * H + 15) / 16) > MLA_MAX_COUNTERS && num_splits != 1)
+    return MLA_E_UNSUPPORTED;
   const int cus = B > 0 ? current_cu_count() : 256;
   if (cus <= 0) return MLA_E_LAUNCH;
   *pl = make_plan(B, P, H, max_kv_len, num_splits, cus);
-  if (pl->S > 0 && (long)B * pl->S > 0x3fffffffL / (8 * pl->RB)) return MLA_E_UNSUPPORTED;
   const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
   const float kvs = fp8 ? kv_scale : 1.f;
   *p = mla_impl::DecodeParams{};
@@ -141,9 +151,8 @@ mla_status setup_decode(const void* q, const void* kv_cache, int kv_dtype, float
   p->H = H;
   p->R = pl->R;
   p->RB = pl->RB;
-  p->S = pl->S;
-  p->chunk_tokens = pl->chunk;
-  p->pairs = B * pl->S;
+  p->W = pl->W;
+  p->seg_steps = kv_dtype == MLA_DTYPE_FP8_E4M3 ? kSegmentStepsFp8 : kSegmentStepsBf16;
   p->score_scale_log2 = softmax_scale * kvs * 1.4426950408889634f;
   p->out_scale = kvs;
   return MLA_OK;
@@ -171,47 +180,17 @@ mla_status mla_verify(const void* q, const void* kv_cache, int kv_dtype, float k
   p.out = out;
   p.out_bf16 = out_dtype == MLA_DTYPE_BF16;
   p.lse = lse;
-  const int N = B * pl.R;
-  if (pl.S > 1) {
+  if (pl.W > 1) {
+    const size_t rows = (size_t)(pl.W + B) * pl.R;
     char* ws = static_cast<char*>(workspace);
+    p.counters = reinterpret_cast<int*>(ws);
+    ws += kCounterBytes;
     p.part_out = reinterpret_cast<float*>(ws);
-    p.part_lse = reinterpret_cast<float*>(
-        ws + align_up((size_t)pl.S * N * MLA_HEAD_DIM_V * sizeof(float)));
-  }
-  hipStream_t stm = static_cast<hipStream_t>(stream);
-  const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
-  if (mla_impl::launch_decode_partial(p, fp8, stm) != hipSuccess) return MLA_E_LAUNCH;
-  if (pl.S > 1 &&
-      mla_impl::launch_merge(p.part_out, p.part_lse, pl.S, N, out, p.out_bf16, lse, stm) !=
-          hipSuccess)
-    return MLA_E_LAUNCH;
-  return MLA_OK;
-}
-
-mla_status mla_verify_partials(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
-                               const int32_t* block_table, int max_blocks_per_seq,
-                               int block_size, const int32_t* seq_lens, const int32_t* kv_begin,
-                               const int32_t* kv_end, int B, int P, int H, int max_kv_len,
-                               float softmax_scale, int num_splits, float* part_out,
-                               float* part_lse, void* stream) {
-  if (B > 0 && (!part_out || !part_lse)) return MLA_E_INVAL;
-  mla_impl::DecodeParams p;
-  Plan pl;
-  mla_status st = setup_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
-                               block_size, seq_lens, kv_begin, kv_end, B, P, H, max_kv_len,
-                               softmax_scale, num_splits, &p, &pl);
-  if (st != MLA_OK) return st;
-  if (B == 0) return MLA_OK;
-  if (pl.S == 1) {  // one split: the kernel writes its normalised rows directly
-    p.out = part_out;
-    p.out_bf16 = 0;
-    p.lse = part_lse;
-  } else {
-    p.part_out = part_out;
-    p.part_lse = part_lse;
+    ws += align_up(rows * MLA_HEAD_DIM_V * sizeof(float));
+    p.part_lse = reinterpret_cast<float*>(ws);
   }
   const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
-  if (mla_impl::launch_decode_partial(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (mla_impl::launch_decode(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)
     return MLA_E_LAUNCH;
   return MLA_OK;
 }

@@ -1,34 +1,43 @@
-// mla_decode.hip -- split-KV decode / speculative-verify kernel and LSE merge for gfx950.
+// mla_decode.hip -- persistent decode / speculative-verify kernel and LSE merge for gfx950.
 //
-// Work decomposition.  One work-group per (sequence b, key split s, 16-row
-// block rb).  A sequence's R = P * H query rows share every latent row it
-// reads (heads attend independently over one shared history, Kimi K3
-// engineering report, section "并行度必须适配真正的形状"), so the grid is sized
-// from key splits: long histories spread over many work-groups, which is what
-// made the 12-head decode fast there, and short verify batches still fill the
-// 256 CUs (same section: 48 work-groups were too few, 384 did better).
+// Work decomposition.  A sequence's R = P * H query rows share every latent row
+// it reads (heads attend independently over one shared history, Kimi K3
+// engineering report, section "并行度必须适配真正的形状"), so the unit of work is
+// a 16-token step of one sequence for one 16-row block.  The steps of all
+// sequences are laid end to end (each sequence also charged a few virtual steps
+// for what a work-group pays per sequence it touches) and cut into W equal
+// pieces; one work-group runs per (piece, row block), about one per CU, so a
+// batch of uneven histories keeps every CU streaming until the end (the same
+// section: the grid must be shaped to the real problem, 48 work-groups were too
+// few, 384 did better).  A sequence spread over several pieces is merged in the
+// same launch: each piece publishes (O / l, lse) for its share with
+// agent-coherent stores and bumps a per-sequence counter; the piece that
+// finishes last combines the shares by lse (the combination position-sharded
+// attention uses, same report, section "缓存可复用，还要能一致地恢复") and resets
+// the counter for the next call.
 //
-// Per work-group, four waves stream disjoint 16-token steps of the split.
+// Per work-group, four waves stream interleaved 16-token steps of a segment.
 // Each wave keeps its own online-softmax state and a 16-row x 512 fp32
-// accumulator, so no wave waits for another until the split is done (the 16
+// accumulator, so no wave waits for another until the segment is done (the 16
 // query rows sit in LDS, read by all four).  Per step:
 //   1. every lane loads 8 (bf16) or 16 (fp8) key values of one token straight
-//      from the paged cache into MFMA A-operand registers (16 B per load;
-//      fp8 is widened to bf16 exactly); a ring of register buffers keeps the
-//      next 2 (fp8) or 1 (bf16) steps in flight;
+//      from the paged cache into MFMA A-operand registers (16 B per load; fp8
+//      is widened to bf16 exactly); a ring of register buffers keeps the next
+//      2 (fp8) or 1 (bf16) steps in flight, and block ids come through the
+//      scalar cache one step early;
 //   2. S^T[16 tokens x 16 rows] = K Q^T with 18 bf16 MFMA 16x16x32 (Q^T, the
 //      B operand, is read from LDS three k-steps ahead of its MFMA);
-//   3. masking and the online softmax run on the 4 scores each lane holds,
+//   3. masking and the softmax numerator run on the 4 scores each lane holds,
 //      with cross-lane max / sum over the 4 lane groups of a row through the
-//      VALU lane swaps (v_permlane16/32_swap, no LDS round trip); the running
-//      max is only moved (and the accumulator rescaled) when it trails the
-//      chunk max by more than 2^8, which keeps the rescale off the hot path;
+//      VALU lane swaps (v_permlane16/32_swap, no LDS round trip); each row's
+//      reference maximum is fixed at its first visible score, so the
+//      accumulator is never rescaled inside the loop (see the step loop);
 //   4. the value part (first 512 dims) of the same registers goes to a per-wave
 //      LDS tile, is read back transposed with ds_read_b64_tr_b16 and feeds
 //      O^T[512 x 16] += V^T P^T with 32 bf16 MFMA 16x16x16; P stays in
 //      registers because the score tile's layout is the B operand's layout.
-// At the end the four waves merge through LDS and the work-group writes either
-// the final rows (one split) or a partial (O_s / l_s, lse_s) for the merge.
+// At the end of a segment the four waves merge through LDS and the work-group
+// writes either the final rows (the piece holds the whole sequence) or its share.
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -41,11 +50,13 @@ constexpr int kWaves = 4;
 constexpr int kStep = 16;       // tokens per wave step
 constexpr int kKSteps = 18;     // 576 / 32
 constexpr int kVRow = 528;      // LDS row stride (bf16) of a wave's value tile (512 + 16 pad)
+constexpr int kQRow = kDK + 8;  // LDS row stride (bf16) of the query rows: 292 dwords, so the
+                                // 16 rows a fragment read touches start in 16 distinct banks
 constexpr int kORow = 516;      // LDS row stride (fp32) of the merged output tile
-constexpr float kSlack = 8.0f;  // log2 units a row's reference max may trail its true max
+constexpr float kCap = 64.0f;   // log2 units a score may exceed its row's reference max
 
 struct DecodeSmem {
-  uint16_t q[16 * kDK];                 // 18,432 B: the row block's queries
+  uint16_t q[16 * kQRow];               // 18,688 B: the row block's queries
   union {
     uint16_t v[kWaves][kStep * kVRow];  // 67,584 B: per-wave value tiles
     struct {
@@ -58,259 +69,503 @@ struct DecodeSmem {
   };
 };
 
-// Dims held by lane group `grp` for k-step kk of the 576-wide contraction.
-// bf16: 8 consecutive dims per k-step; fp8: one 16-byte load covers two
-// k-steps.  The same map is used for keys and queries, so any permutation of
-// the contraction index is fine.
-template <bool kFp8>
+// Dims held by lane group `grp` for k-step kk of the 576-wide contraction: a
+// pair of k-steps covers 16 consecutive dims per lane (one 16-byte load of fp8
+// codes, two of bf16).  The same map is used for keys and queries, so any
+// permutation of the contraction index is fine.
 __device__ __forceinline__ int kdim(int kk, int grp) {
-  return kFp8 ? 64 * (kk >> 1) + 16 * grp + 8 * (kk & 1) : 32 * kk + 8 * grp;
+  return 64 * (kk >> 1) + 16 * grp + 8 * (kk & 1);
+}
+
+// The value tile of a wave is token-major with the 16-byte chunks of rows
+// 8..15 swapped pairwise (chunk c stored at c ^ 1): a fragment write (16 rows,
+// one chunk) then covers all 64 banks, and a transposed read (4 rows of one
+// half) stays conflict-free.
+// Four consecutive output values of row n, fp32 or bf16.
+__device__ __forceinline__ void store_row4(const DecodeParams& p, size_t n, int d, f32x4 v) {
+  if (p.out_bf16) {
+    const bf16x4 o = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
+    *(bf16x4*)((uint16_t*)p.out + n * kDV + d) = o;
+  } else {
+    *(f32x4*)((float*)p.out + n * kDV + d) = v;
+  }
+}
+
+// int32 in the constant address space: a uniform index reads it with a scalar load.
+typedef __attribute__((address_space(4))) const int32_t kconst_i32;
+
+// Key range of sequence b this call covers, in 16-token steps from `base`.
+struct SeqRange {
+  int L, lo, hi, base, n;
+};
+
+__device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
+  SeqRange r;
+  r.L = ((const kconst_i32*)p.seq_lens)[b];
+  r.lo = p.kv_begin ? max(((const kconst_i32*)p.kv_begin)[b], 0) : 0;
+  r.hi = p.kv_end ? min(((const kconst_i32*)p.kv_end)[b], r.L) : r.L;
+  r.base = r.lo & ~(kStep - 1);
+  r.n = r.hi > r.lo ? (r.hi - r.base + kStep - 1) / kStep : 0;
+  return r;
+}
+
+// Work-group w of W owns steps [first_step(w), first_step(w + 1)) of the batch's
+// concatenated step list; step s belongs to owner(s).
+__device__ __forceinline__ long first_step(long w, long N, int W) { return w * N / W; }
+__device__ __forceinline__ int owner(long s, long N, int W) {
+  return (int)(((s + 1) * W - 1) / N);
+}
+
+// Max / sum over the 16 lanes of a row group (lanes 16 g .. 16 g + 15).
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Last piece of sequence b: combine the partials of pieces w_first..w_last for
+// row rr (16 threads per row, 4 dims each per 64-dim slab).  The lse of all pieces
+// are read in parallel (one piece per lane), the partial rows four pieces at a
+// time; a piece that saw no key of the row has lse = -inf and an unwritten row,
+// which its zero weight selects away.
+__device__ __forceinline__ void merge_pieces(const DecodeParams& p, int b, int rr, size_t n,
+                                             int w_first, int w_last) {
+  const int j = threadIdx.x & 15;
+  const size_t R = p.R;
+  const float* lse_b = p.part_lse + (size_t)b * R + rr;  // slot v at v * R
+  // slot v's rows start at part_out + (v + b) * R * 512; this lane's bytes within it
+  const uint32_t off = (uint32_t)(rr * kDV + 4 * j) * 4;
+  float mx = -INFINITY;
+  for (int v = w_first + j; v <= w_last; v += 16) mx = fmaxf(mx, load_agent(lse_b + v * R));
+  mx = max16(mx);
+  f32x4 o8[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) o8[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  float ls = 0.f;
+  if (mx != -INFINITY) {
+    for (int v = w_first + j; v <= w_last; v += 16) {
+      const float x = load_agent(lse_b + v * R);
+      ls += (x == -INFINITY) ? 0.f : expf(x - mx);
+    }
+    ls = sum16(ls);
+    for (int v0 = w_first; v0 <= w_last; v0 += 4) {
+      float wt[4];
+      f32x4 x[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int v = min(v0 + u, w_last);  // past the end: re-read the last slot, weight 0
+        const float l = load_agent(lse_b + v * R);
+        wt[u] = (v0 + u <= w_last && l != -INFINITY) ? expf(l - mx) : 0.f;
+        const auto rsrc = agent_rsrc(p.part_out + (size_t)(v + b) * R * kDV);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) x[u][k] = load_agent16(rsrc, off + 256 * k);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const f32x4 t = wt[u] * x[u][k];
+          if (wt[u] > 0.f) o8[k] += t;
+        }
+    }
+    const float il = 1.f / ls;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o8[k] *= il;
+  }
+#pragma unroll
+  for (int k = 0; k < 8; ++k) store_row4(p, n, 4 * j + 64 * k, o8[k]);
+  if (p.lse && j == 0) p.lse[n] = (mx == -INFINITY) ? -INFINITY : mx + logf(ls);
+}
+
+// Sum over the work-group (256 threads); sh holds 4 values and is free on entry.
+__device__ __forceinline__ long long block_sum(long long v, long long* sh) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = v;
+  __syncthreads();
+  const long long t = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return t;
+}
+
+// Exclusive prefix sum over the work-group in thread order; *total gets the sum.
+__device__ __forceinline__ long long block_exclusive_scan(long long v, long long* sh,
+                                                          long long* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  long long incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const long long t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  long long before = 0;
+  for (int i = 0; i < wave; ++i) before += sh[i];
+  *total = sh[0] + sh[1] + sh[2] + sh[3];
+  __syncthreads();
+  return before + incl - v;
 }
 
 template <bool kFp8>
-__global__ __launch_bounds__(256, 1) void decode_partial_kernel(const DecodeParams p) {
+__global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
   __shared__ __attribute__((aligned(16))) DecodeSmem sm;
+  __shared__ int last_flag;
   constexpr int kLoads = kFp8 ? 9 : 18;  // 16-byte loads per lane per step
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;  // token (A rows) / query row (B, C columns)
   const int grp = lane >> 4;  // k-group (A, B) / 4-row group (C)
-
-  // Work-group -> (sequence, split, row block).  The RB row blocks of one
-  // (b, s) pair get ids congruent mod 8, so they land on one XCD and share its L2.
+  // Work-group -> (piece, row block).  The RB row blocks of one piece get ids
+  // congruent mod 8, so they run on one XCD and read the piece's rows through
+  // one L2.
+  const int W = p.W;
   const int per = 8 * p.RB;
-  const int id = blockIdx.x;
-  const int rb = (id % per) / 8;
-  const int pair = (id / per) * 8 + (id % 8);
-  if (pair >= p.pairs) return;
-  const int b = pair / p.S;
-  const int s = pair % p.S;
-
-  const int L = p.seq_lens[b];
-  const int lo = p.kv_begin ? max(p.kv_begin[b], 0) : 0;
-  const int hi_all = p.kv_end ? min(p.kv_end[b], L) : L;
-  const int base = lo & ~(kStep - 1);
-  const int t_begin = base + s * p.chunk_tokens;
-  const int t_end = (s == p.S - 1) ? hi_all : min(hi_all, t_begin + p.chunk_tokens);
-
-  const int r = rb * 16 + col;
-  const bool row_ok = r < p.R;
-  const int hi_row = row_ok ? min(hi_all, L - p.P + r / p.H + 1) : lo;
-
-  // The row block's queries go to LDS once (rows past R are zero); every step
-  // reads its Q^T fragments (B operand of the score MFMA) from there, three
-  // k-steps ahead of their MFMA, which keeps the 16 query rows out of the
-  // register budget.
-  for (int i = tid; i < 16 * (kDK / 8); i += 256) {
-    const int row = i / (kDK / 8), c8 = i % (kDK / 8);
-    const int rq = rb * 16 + row;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (rq < p.R) v = *(const u32x4*)(p.q + ((size_t)b * p.R + rq) * kDK + 8 * c8);
-    *(u32x4*)(sm.q + row * kDK + 8 * c8) = v;
-  }
-  __syncthreads();
-  const uint16_t* qsrc = sm.q + col * kDK;
-  auto qfrag = [&](int kk) { return *(const bf16x8*)(qsrc + kdim<kFp8>(kk, grp)); };
-
-  f32x4 acc[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  uint16_t* vt = sm.v[wave];
+  const int rb = (blockIdx.x % per) / 8;
+  const int w = (blockIdx.x / per) * 8 + blockIdx.x % 8;
+  if (w >= W) return;
   const size_t row_bytes = kFp8 ? kDK : 2 * kDK;
+  uint16_t* vt = sm.v[wave];
 
-  auto load_step = [&](int t0, u32x4* dst) {
-    // all 16 tokens of an aligned step sit in one block; clamp into the visible
-    // span so masked lanes read a real row of that block, never a poisoned slot
-    const int blk = p.block_table[(size_t)b * p.max_blocks + t0 / p.block_size];
-    const int t = min(max(t0 + col, lo), hi_all - 1);
-    const uint8_t* krow = p.kv + ((size_t)blk * p.block_size + (t % p.block_size)) * row_bytes;
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i)
-      dst[i] = *(const u32x4*)(krow + (kFp8 ? 64 * i + 16 * grp : 2 * (32 * i + 8 * grp)));
-  };
-
-  auto process_step = [&](const u32x4* raw, int t0) {
-    // scores: lane (col, grp) gets tokens t0 + 4 * grp + i of query row `col`; the value
-    // part of each fragment goes to this wave's LDS tile on the way (bf16, token-major).
-    // Schedule: the Q^T fragments of three k-steps are read before the first MFMA,
-    // then every MFMA is followed by the read of the fragment three steps later.
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-    uint16_t* vrow = vt + col * kVRow;
-    if constexpr (kFp8) {
-#pragma unroll
-      for (int j = 0; j < 9; ++j) {
-        bf16x8 ka, kb;
-        fp8x16_to_bf16(raw[j], ka, kb);
-        if (j < 8) {
-          *(bf16x8*)(vrow + 64 * j + 16 * grp) = ka;
-          *(bf16x8*)(vrow + 64 * j + 16 * grp + 8) = kb;
-        }
-        sc = mfma_16x16x32(ka, qfrag(2 * j), sc);
-        sc = mfma_16x16x32(kb, qfrag(2 * j + 1), sc);
-      }
-    } else {
-#pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        const bf16x8 k = __builtin_bit_cast(bf16x8, raw[kk]);
-        if (kk < 16) *(bf16x8*)(vrow + 32 * kk + 8 * grp) = k;
-        sc = mfma_16x16x32(k, qfrag(kk), sc);
+  // ---- the batch's step list: total N and where this piece starts ----
+  // Each sequence with keys contributes p.seg_steps virtual steps followed by its
+  // real 16-token steps; pieces are equal shares of that list.  The virtual steps
+  // stand for what a piece pays per sequence it touches (query load, wave merge,
+  // publishing a partial), so a piece that picks up a second sequence gets that
+  // much less streaming.  256 sequences are read at a time, one per thread.
+  // Piece 0 also writes the rows of sequences without visible keys: zeros and
+  // lse = -inf.
+  __shared__ long long red[kWaves];
+  __shared__ long long seg[2];  // first sequence of the piece, its offset in the list
+  const int c = p.seg_steps;
+  long long part = 0;
+  for (int b0 = 0; b0 < p.B; b0 += 256) {
+    const int b = b0 + tid;
+    if (b >= p.B) break;
+    const int nb = seq_range(p, b).n;
+    part += nb > 0 ? nb + c : 0;
+    if (w == 0 && nb == 0) {
+      for (int row = 0; row < 16; ++row) {
+        const int rr = rb * 16 + row;
+        if (rr >= p.R) break;
+        const size_t n = (size_t)b * p.R + rr;
+        for (int d = 0; d < kDV; d += 4) store_row4(p, n, d, (f32x4){0.f, 0.f, 0.f, 0.f});
+        if (p.lse) p.lse[n] = -INFINITY;
       }
     }
-
-    {
-      constexpr int kDsRead = 0x100, kMfma = 0x8, kAhead = 3;
-      __builtin_amdgcn_sched_group_barrier(kDsRead, kAhead, 0);
-#pragma unroll
-      for (int i = 0; i < kKSteps - kAhead; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+  if (tid == 0) seg[0] = p.B;
+  const long long N = block_sum(part, red);
+  // With fewer list entries than pieces only the first N pieces take part, so every
+  // piece in use holds at least one entry: the pieces that share a sequence's real
+  // steps are consecutive and each holds some of them.
+  const int We = (int)min((long long)W, N);
+  if (w >= We) return;
+  const long S0 = first_step(w, N, We), S1 = first_step(w + 1, N, We);
+  {
+    long long carry = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 256) {
+      const int b = b0 + tid;
+      const int nb = b < p.B ? seq_range(p, b).n : 0;
+      const long long mb = nb > 0 ? nb + c : 0;
+      long long tot;
+      const long long ob = carry + block_exclusive_scan(mb, red, &tot);
+      if (mb > 0 && ob <= S0 && S0 < ob + mb) {  // the one sequence holding entry S0
+        seg[0] = b;
+        seg[1] = ob;
       }
-      __builtin_amdgcn_sched_group_barrier(kMfma, kAhead, 0);
+      carry += tot;
+      __syncthreads();
+      if (seg[0] < p.B) break;
     }
+  }
+  const int b_first = (int)seg[0];
+  long o = (long)seg[1];  // list offset of sequence b
 
-    float sv[4];
-    float cm = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int t = t0 + 4 * grp + i;
-      const bool vis = (t >= lo) && (t < hi_row);
-      sv[i] = vis ? sc[i] * p.score_scale_log2 : -INFINITY;
-      cm = fmaxf(cm, sv[i]);
-    }
-    cm = wave_max16x4(cm);
-    const float mn = fmaxf(m_run, cm);
-    const bool need = mn > m_run + kSlack;
-    if (__builtin_amdgcn_ballot_w64(need)) {
-      const float alpha = need ? fast_exp2(m_run - mn) : 1.f;
-      if (need) m_run = mn;
-      l_run *= alpha;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] *= alpha;
-    }
-    const float mref = (m_run == -INFINITY) ? 0.f : m_run;
-    float pv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      pv[i] = fast_exp2(sv[i] - mref);
-      l_run += pv[i];
-    }
-    const bf16x4 pb = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
-    const i16x4 pf = __builtin_bit_cast(i16x4, pb);
+  for (int b = b_first; b < p.B && o < S1; ++b) {
+    const SeqRange sr = seq_range(p, b);
+    if (sr.n == 0) continue;  // empty sequences were written above
+    const long rs = o + c;    // list offset of b's first real step
+    o = rs + sr.n;
+    const int a = (int)(max(S0, rs) - rs), e = (int)(min(S1, rs + sr.n) - rs);  // local steps
+    if (e <= a) continue;  // only virtual entries of b fall in this piece
+    const int lo = sr.lo, hi_all = sr.hi, L = sr.L;
+    const int r = rb * 16 + col;
+    const bool row_ok = r < p.R;
+    const int hi_row = row_ok ? min(hi_all, L - p.P + r / p.H + 1) : lo;
+    const int w_first = owner(rs, N, We), w_last = owner(rs + sr.n - 1, N, We);
 
-    wave_lds_fence();
-    const uint16_t* vsrc = vt + (4 * grp + (col >> 2)) * kVRow + 4 * (col & 3);
-#pragma unroll
-    for (int m = 0; m < 32; ++m) {
-      acc[m] = mfma_16x16x16(lds_read_tr16(vsrc + 16 * m), pf, acc[m]);
-    }
-    wave_lds_fence();
-  };
-
-  // A ring of kDepth register buffers per wave: the loads of the next kDepth - 1
-  // steps are in flight while a step computes (one step moves 9 KB of fp8 or
-  // 18 KB of bf16 rows per wave).  The loop is unrolled by kDepth so every buffer
-  // index is a compile-time constant.
-  constexpr int kDepth = kFp8 ? 3 : 2;
-  constexpr int kStride = kStep * kWaves;
-  const int t_first = t_begin + kStep * wave;
-  const int n_steps = t_first < t_end ? (t_end - t_first + kStride - 1) / kStride : 0;
-  // Every step issues the same loads (prefetches past the wave's last step re-read
-  // that step), and the steady-state loop below has no branch around them, so the
-  // compiler counts them exactly and keeps the whole ring in flight.
-  u32x4 ring[kDepth][kLoads];
-  const int last_t0 = t_first + (n_steps - 1) * kStride;
-  if (n_steps > 0) {
-#pragma unroll
-    for (int u = 0; u < kDepth - 1; ++u) load_step(min(t_first + u * kStride, last_t0), ring[u]);
-  }
-  int i0 = 0;
-  for (; i0 + kDepth <= n_steps; i0 += kDepth) {
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const int i = i0 + u;
-      load_step(min(t_first + (i + kDepth - 1) * kStride, last_t0),
-                ring[(u + kDepth - 1) % kDepth]);
-      __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the step computes
-      process_step(ring[u], t_first + i * kStride);
-    }
-  }
-  // tail: fewer than kDepth steps remain and all of them are already loaded
-#pragma unroll
-  for (int u = 0; u < kDepth - 1; ++u)
-    if (i0 + u < n_steps) process_step(ring[u], t_first + (i0 + u) * kStride);
-
-  // ---- merge the four waves ----
-  const float l_row = wave_sum16x4(l_run);
-  __syncthreads();  // value tiles are dead from here on; the union is reused
-  if (grp == 0) {
-    sm.red.m[wave][col] = m_run;
-    sm.red.l[wave][col] = l_row;
-  }
-  __syncthreads();
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.red.m[w][col]);
-  float Lsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const float mw = sm.red.m[w][col];
-    if (mw != -INFINITY) Lsum += sm.red.l[w][col] * fast_exp2(mw - M);
-  }
-  const float my_scale = (m_run == -INFINITY) ? 0.f : fast_exp2(m_run - M);
-  if (wave == 0 && grp == 0) {
-    sm.red.row_m[col] = M;
-    sm.red.row_l[col] = Lsum;
-  }
-  // acc[m][i] = O[row col][dim 16 m + 4 grp + i]
-  float* orow = sm.red.o + col * kORow + 4 * grp;
-  for (int w = 0; w < kWaves; ++w) {
-    if (wave == w) {
-#pragma unroll
-      for (int m = 0; m < 32; ++m) {
-        f32x4 v = acc[m] * my_scale;
-        if (w > 0) v += *(const f32x4*)(orow + 16 * m);
-        *(f32x4*)(orow + 16 * m) = v;
-      }
+    __syncthreads();  // the previous segment is done with the LDS tiles
+    // The row block's queries go to LDS once per segment (rows past R are zero);
+    // every step reads its Q^T fragments (B operand of the score MFMA) from there,
+    // three k-steps ahead of their MFMA, which keeps the 16 query rows out of the
+    // register budget.
+    for (int i = tid; i < 16 * (kDK / 8); i += 256) {
+      const int row = i / (kDK / 8), c8 = i % (kDK / 8);
+      const int rq = rb * 16 + row;
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (rq < p.R) v = *(const u32x4*)(p.q + ((size_t)b * p.R + rq) * kDK + 8 * c8);
+      *(u32x4*)(sm.q + row * kQRow + 8 * c8) = v;
     }
     __syncthreads();
-  }
+    const uint16_t* qsrc = sm.q + col * kQRow;
+    auto qfrag = [&](int kk) { return *(const bf16x8*)(qsrc + kdim(kk, grp)); };
 
-  const int orow_i = tid >> 4;  // 16 threads per output row
-  const int rr = rb * 16 + orow_i;
-  if (rr >= p.R) return;
-  const float Mr = sm.red.row_m[orow_i];
-  const float Lr = sm.red.row_l[orow_i];
-  const float inv = (Lr > 0.f) ? p.out_scale / Lr : 0.f;
-  const float lse_v = (Lr > 0.f) ? (Mr + fast_log2(Lr)) * kLn2 : -INFINITY;
-  const size_t n = (size_t)b * p.R + rr;
-  const float* src = sm.red.o + orow_i * kORow;
-  if (p.S == 1) {
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int d = 4 * (tid & 15) + 64 * k;
-      const f32x4 v = *(const f32x4*)(src + d) * inv;
-      if (p.out_bf16) {
-        const bf16x4 o = {(__bf16)v.x, (__bf16)v.y, (__bf16)v.z, (__bf16)v.w};
-        *(bf16x4*)((uint16_t*)p.out + n * kDV + d) = o;
+    // Online softmax with a reference max that never moves inside the step loop.
+    // A row's reference m_ref is its first visible score maximum (until then its
+    // accumulator is zero, so setting it needs no rescale); later scores enter as
+    // 2^(s - m_ref), which bf16 and fp32 hold exactly in range up to 2^kCap.  The
+    // exponent is capped there, and m_max tracks the true maximum: a wave in which
+    // some row went more than kCap above its reference runs its steps again with
+    // the true maximum as reference (no score can exceed it then).  Keeping the
+    // accumulator free of a data-dependent rescale keeps it in place in the
+    // accumulation registers for the whole loop.
+    f32x4 acc[32];
+    float m_ref = -INFINITY;
+    float m_max = -INFINITY;
+    float l_run = 0.f;
+
+    // Cache row of token t0 of an aligned step.  t0 is uniform, so the block id comes
+    // through the scalar cache and stays out of the vector-load queue: a vector load
+    // here would make every later wait on it drain the whole prefetch ring.
+    const kconst_i32* bt = (const kconst_i32*)(p.block_table + (size_t)b * p.max_blocks);
+    auto step_row = [&](int t0) -> long {
+      t0 = __builtin_amdgcn_readfirstlane(t0);
+      return (long)bt[t0 / p.block_size] * p.block_size + t0 % p.block_size;
+    };
+    auto load_step = [&](long row0, int t0, u32x4* dst) {
+      // all 16 tokens of an aligned step sit in one block; clamping into the visible
+      // span keeps every lane inside the step, on a real row, never a poisoned slot
+      const int t = min(max(t0 + col, lo), hi_all - 1);
+      const uint8_t* krow = p.kv + row0 * row_bytes + (t - t0) * (int)row_bytes;
+  #pragma unroll
+      for (int i = 0; i < kLoads; ++i)
+        dst[i] = *(const u32x4*)(krow + (kFp8 ? 64 * i + 16 * grp : 2 * kdim(i, grp)));
+    };
+
+    auto process_step = [&](const u32x4* raw, int t0) {
+      // scores: lane (col, grp) gets tokens t0 + 4 * grp + i of query row `col`; the value
+      // part of each fragment goes to this wave's LDS tile on the way (bf16, token-major).
+      // Schedule: the Q^T fragments of three k-steps are read before the first MFMA,
+      // then every MFMA is followed by the read of the fragment three steps later.
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      // write bases: chunk 8 j + 2 grp + h of row col sits at chunk (8 j + 2 grp + (h ^ sw))
+      const int sw = (col >> 3) & 1;
+      uint16_t* vrow0 = vt + col * kVRow + 16 * grp + 8 * sw;        // h = 0
+      uint16_t* vrow1 = vt + col * kVRow + 16 * grp + 8 * (sw ^ 1);  // h = 1
+      if constexpr (kFp8) {
+  #pragma unroll
+        for (int j = 0; j < 9; ++j) {
+          bf16x8 ka, kb;
+          fp8x16_to_bf16(raw[j], ka, kb);
+          if (j < 8) {  // dims 64 j + 16 grp .. + 15 are chunks 8 j + 2 grp, + 1
+            *(bf16x8*)(vrow0 + 64 * j) = ka;
+            *(bf16x8*)(vrow1 + 64 * j) = kb;
+          }
+          sc = mfma_16x16x32(ka, qfrag(2 * j), sc);
+          sc = mfma_16x16x32(kb, qfrag(2 * j + 1), sc);
+        }
       } else {
-        *(f32x4*)((float*)p.out + n * kDV + d) = v;
+  #pragma unroll
+        for (int kk = 0; kk < kKSteps; ++kk) {
+          const bf16x8 k = __builtin_bit_cast(bf16x8, raw[kk]);
+          if (kk < 16) *(bf16x8*)(((kk & 1) ? vrow1 : vrow0) + 64 * (kk >> 1)) = k;
+          sc = mfma_16x16x32(k, qfrag(kk), sc);
+        }
+      }
+
+      {
+        constexpr int kDsRead = 0x100, kMfma = 0x8, kAhead = 3;
+        __builtin_amdgcn_sched_group_barrier(kDsRead, kAhead, 0);
+  #pragma unroll
+        for (int i = 0; i < kKSteps - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kMfma, kAhead, 0);
+      }
+
+      float sv[4];
+      float cm = -INFINITY;
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + 4 * grp + i;
+        const bool vis = (t >= lo) && (t < hi_row);
+        sv[i] = vis ? sc[i] * p.score_scale_log2 : -INFINITY;
+        cm = fmaxf(cm, sv[i]);
+      }
+      cm = wave_max16x4(cm);
+      m_max = fmaxf(m_max, cm);
+      m_ref = (m_ref == -INFINITY) ? cm : m_ref;
+      const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float pv[4];
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pv[i] = fast_exp2(fminf(sv[i] - mref, kCap));
+        l_run += pv[i];
+      }
+      const bf16x4 pb = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+      const i16x4 pf = __builtin_bit_cast(i16x4, pb);
+
+      wave_lds_fence();
+      // lane (col, grp) addresses token 4 grp + col / 4, dims 16 m + 4 (col % 4) .. + 3
+      const int vr = 4 * grp + (col >> 2);
+      const uint16_t* vsrc =
+          vt + vr * kVRow + 8 * (((col & 3) >> 1) ^ ((vr >> 3) & 1)) + 4 * (col & 1);
+  #pragma unroll
+      for (int m = 0; m < 32; ++m) acc[m] = mfma_16x16x16(lds_read_tr16(vsrc + 16 * m), pf, acc[m]);
+      {
+        // each transposed read runs four MFMAs ahead of its use: enough to cover the LDS
+        // latency without parking 32 fragments in registers
+        constexpr int kDsRead = 0x100, kMfma = 0x8, kAhead = 4;
+        __builtin_amdgcn_sched_group_barrier(kDsRead, kAhead, 0);
+  #pragma unroll
+        for (int i = 0; i < 32 - kAhead; ++i) {
+          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kMfma, kAhead, 0);
+      }
+      wave_lds_fence();
+    };
+
+    // A ring of kDepth register buffers per wave: the loads of the next kDepth - 1
+    // steps are in flight while a step computes (one step moves 9 KB of fp8 or
+    // 18 KB of bf16 rows per wave).  The loop is unrolled by kDepth so every buffer
+    // index is a compile-time constant.
+    constexpr int kDepth = kFp8 ? 3 : 2;
+    constexpr int kStride = kStep * kWaves;
+    const int t_first = sr.base + kStep * (a + wave);
+    const int n_steps = a + wave < e ? (e - a - wave + kWaves - 1) / kWaves : 0;
+    // Every step issues the same loads (prefetches past the wave's last step re-read
+    // that step), and the steady-state loop below has no branch around them, so the
+    // compiler counts them exactly and keeps the whole ring in flight.
+    u32x4 ring[kDepth][kLoads];
+    const int last_t0 = t_first + (n_steps - 1) * kStride;
+    auto step_t0 = [&](int i) { return min(t_first + i * kStride, last_t0); };
+    for (int pass = 0; pass < 2; ++pass) {
+  #pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    l_run = 0.f;
+    long row_next = 0;  // cache row of the step the next prefetch loads (read a step early)
+    if (n_steps > 0) {
+  #pragma unroll
+      for (int u = 0; u < kDepth - 1; ++u) load_step(step_row(step_t0(u)), step_t0(u), ring[u]);
+      row_next = step_row(step_t0(kDepth - 1));
+    }
+    int i0 = 0;
+    for (; i0 + kDepth <= n_steps; i0 += kDepth) {
+  #pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int i = i0 + u;
+        load_step(row_next, step_t0(i + kDepth - 1), ring[(u + kDepth - 1) % kDepth]);
+        row_next = step_row(step_t0(i + kDepth));
+        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the step computes
+        process_step(ring[u], t_first + i * kStride);
       }
     }
-    if (p.lse && (tid & 15) == 0) p.lse[n] = lse_v;
-  } else {
-    const size_t pn = (size_t)s * p.B * p.R + n;
-    if ((tid & 15) == 0) p.part_lse[pn] = lse_v;
-    if (Lr > 0.f) {
+    // tail: fewer than kDepth steps remain and all of them are already loaded
+  #pragma unroll
+    for (int u = 0; u < kDepth - 1; ++u)
+      if (i0 + u < n_steps) process_step(ring[u], t_first + (i0 + u) * kStride);
+    // a row beyond its cap: run the steps again from its true maximum
+    if (!__builtin_amdgcn_ballot_w64(m_max > m_ref + kCap)) break;
+    m_ref = m_max;
+    }
+
+    // ---- merge the four waves ----
+    const float l_row = wave_sum16x4(l_run);
+    __syncthreads();  // value tiles are dead from here on; the union is reused
+    if (grp == 0) {
+      sm.red.m[wave][col] = m_ref;
+      sm.red.l[wave][col] = l_row;
+    }
+    __syncthreads();
+    float M = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int d = 4 * (tid & 15) + 64 * k;
-        *(f32x4*)(p.part_out + pn * kDV + d) = *(const f32x4*)(src + d) * inv;
+    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm.red.m[v][col]);
+    float Lsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float mv = sm.red.m[v][col];
+      if (mv != -INFINITY) Lsum += sm.red.l[v][col] * fast_exp2(mv - M);
+    }
+    const float my_scale = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - M);
+    if (wave == 0 && grp == 0) {
+      sm.red.row_m[col] = M;
+      sm.red.row_l[col] = Lsum;
+    }
+    // acc[m][i] = O[row col][dim 16 m + 4 grp + i]
+    float* orow = sm.red.o + col * kORow + 4 * grp;
+    for (int v = 0; v < kWaves; ++v) {
+      if (wave == v) {
+#pragma unroll
+        for (int m = 0; m < 32; ++m) {
+          f32x4 x = acc[m] * my_scale;
+          if (v > 0) x += *(const f32x4*)(orow + 16 * m);
+          *(f32x4*)(orow + 16 * m) = x;
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- this piece's result for sequence b: final rows, or a partial + merge ----
+    const int orow_i = tid >> 4;  // 16 threads per output row
+    const int rr = rb * 16 + orow_i;
+    const bool rr_ok = rr < p.R;
+    const float Mr = sm.red.row_m[orow_i];
+    const float Lr = sm.red.row_l[orow_i];
+    const float inv = (Lr > 0.f) ? p.out_scale / Lr : 0.f;
+    const float lse_v = (Lr > 0.f) ? (Mr + fast_log2(Lr)) * kLn2 : -INFINITY;
+    const size_t n = (size_t)b * p.R + rr;
+    const float* src = sm.red.o + orow_i * kORow;
+    if (w_first == w_last) {  // this piece holds the whole sequence
+      if (rr_ok) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int d = 4 * (tid & 15) + 64 * k;
+          store_row4(p, n, d, *(const f32x4*)(src + d) * inv);
+        }
+        if (p.lse && (tid & 15) == 0) p.lse[n] = lse_v;
+      }
+      continue;
+    }
+    const size_t slot = (size_t)(w + b) * p.R;  // slot w + b is unique per (piece, sequence)
+    if (rr_ok) {
+      if ((tid & 15) == 0) store_agent(p.part_lse + slot + rr, lse_v);
+      if (Lr > 0.f) {
+        const auto rsrc = agent_rsrc(p.part_out + slot * kDV);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int d = 4 * (tid & 15) + 64 * k;
+          store_agent16(rsrc, (uint32_t)(rr * kDV + d) * 4, *(const f32x4*)(src + d) * inv);
+        }
       }
     }
+    // Publish the partial; the last piece to finish sequence b merges all of them.
+    // Every thread waits for its agent-coherent stores to be acknowledged before
+    // the barrier, so they are visible device-wide before the counter moves; the
+    // merging piece reads them with agent-coherent loads.  No fence, hence no
+    // writeback or invalidation of the XCD's L2.
+    wait_vm_all();
+    __syncthreads();
+    if (tid == 0) {
+      int* cnt = p.counters + b * p.RB + rb;
+      const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const int last = done == w_last - w_first;
+      if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      last_flag = last;
+    }
+    __syncthreads();
+    if (!last_flag) continue;
+    if (rr_ok) merge_pieces(p, b, rr, n, w_first, w_last);
   }
 }
 
@@ -349,15 +604,15 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
 
 }  // namespace
 
-int decode_grid_size(int pairs, int RB) { return ((pairs + 7) / 8) * 8 * RB; }
+int decode_grid_size(int W, int RB) { return ((W + 7) / 8) * 8 * RB; }
 
-hipError_t launch_decode_partial(const DecodeParams& p, bool kv_fp8, hipStream_t stream) {
-  const int grid = decode_grid_size(p.pairs, p.RB);
+hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream) {
+  const int grid = decode_grid_size(p.W, p.RB);
   if (grid == 0) return hipSuccess;
   if (kv_fp8)
-    hipLaunchKernelGGL(decode_partial_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(decode_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL(decode_partial_kernel<false>, dim3(grid), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -131,6 +131,38 @@ __device__ __forceinline__ float wave_sum_xor32(float v) {
 
 // Keep the compiler from moving LDS accesses across this point; lanes of one
 // wave exchange data through LDS around it.
+// Agent-coherent global accesses without fences.  On gfx950 the L2 is per XCD;
+// a relaxed agent-scope atomic store or load is issued with the sc1 cache bit,
+// which writes through to / reads from the device-coherent level, while a
+// release or acquire fence would write back or invalidate the whole XCD's L2.
+__device__ __forceinline__ void store_agent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_agent(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte agent-coherent accesses through a buffer resource: `base` is uniform
+// across the wave, `off` a per-lane byte offset (raw buffer, 2^31 - 1 bytes).
+constexpr int kCachePolicySc1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t agent_rsrc(float* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, 0x7fffffff, 0x00020000);
+}
+__device__ __forceinline__ f32x4 load_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCachePolicySc1));
+}
+__device__ __forceinline__ void store_agent16(__amdgpu_buffer_rsrc_t r, uint32_t off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCachePolicySc1);
+}
+
+// Wait until every vector memory access this wave issued has completed (for
+// stores: acknowledged at the level their cache bits name).  The signal fences
+// keep the compiler from moving memory accesses across the wait.
+__device__ __forceinline__ void wait_vm_all() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt = 0, other counters free
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -7,9 +7,11 @@
 
 namespace mla_impl {
 
-// Split-KV decode / verify over a paged latent cache.  One work-group per
-// (sequence, key split, 16-row block); four waves per work-group, each wave
-// streaming its own 16-token steps of the split.
+// Decode / verify over a paged latent cache in one persistent launch: the
+// batch's key ranges, cut into 16-token steps and concatenated, are divided into
+// W equal pieces; work-group (piece w, 16-row block rb) walks the sequence
+// segments of its piece, and the last piece to finish a sequence merges that
+// sequence's partials.
 struct DecodeParams {
   const uint16_t* q;           // [B, R, 576] bf16, R = P * H
   const uint8_t* kv;           // [num_blocks, block_size, 576] bf16 or fp8 codes
@@ -20,22 +22,22 @@ struct DecodeParams {
   int max_blocks;
   int block_size;              // multiple of 16
   int B, P, H, R, RB;          // RB = ceil(R / 16)
-  int S;                       // splits per sequence
-  int chunk_tokens;            // tokens per split (multiple of 64); the last split takes the rest
-  int pairs;                   // B * S
+  int W;                       // pieces of the concatenated step list
+  int seg_steps;               // virtual steps charged per sequence a piece touches
   float score_scale_log2;      // softmax_scale * kv_scale * log2(e)
   float out_scale;             // kv_scale for fp8 caches, 1 for bf16
-  float* part_out;             // S > 1: [S, B * R, 512]
-  float* part_lse;             // S > 1: [S, B * R]
-  void* out;                   // S == 1: [B * R, 512] fp32 or bf16
+  float* part_out;             // [W + B, R, 512]: slot w + b holds piece w's share of sequence b
+  float* part_lse;             // [W + B, R]
+  int* counters;               // [B, RB] (B * RB <= MLA_MAX_COUNTERS): zero on entry, left zero
+  void* out;                   // [B * R, 512] fp32 or bf16
   int out_bf16;
-  float* lse;                  // S == 1: [B * R] or null
+  float* lse;                  // [B * R] or null
 };
 
-// Number of work-groups launch_decode_partial uses.
-int decode_grid_size(int pairs, int RB);
+// Work-groups launch_decode uses for W pieces and RB row blocks.
+int decode_grid_size(int W, int RB);
 
-hipError_t launch_decode_partial(const DecodeParams& p, bool kv_fp8, hipStream_t stream);
+hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream);
 
 hipError_t launch_merge(const float* part_out, const float* part_lse, int S, int N, void* out,
                         int out_bf16, float* lse, hipStream_t stream);

@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["mla_decode", "mla_verify", "mla_verify_partials", "mla_prefill", "mla_merge_lse",
+    for n in ["mla_decode", "mla_verify", "mla_prefill", "mla_merge_lse",
               "mla_decode_workspace_size", "mla_decode_num_splits", "mla_status_string",
               "mla_version"]:
         assert n in names
@@ -113,8 +113,8 @@ def test_prefill_rejects_bad_arguments(lib):
 
 def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
     """The pages' short verify: one sequence, 4 positions, 12 heads; 48 work-groups were
-    too few for the chip and 384 did better.  The split plan gives at least 384 work-groups
-    and at least one per CU once the history is long enough to split."""
+    too few for the chip.  The persistent plan puts one work-group on every CU (minus
+    the rounding of CUs to whole row-block groups) once the history is long enough."""
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_closed_forms.json")))
     sv = g["short_verify_workgroups"]
     heads = sv["heads"]
@@ -122,22 +122,45 @@ def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
     assert heads * sv["tiled_width"] // sv["narrow_tile_columns"] == sv["narrow_tile_workgroups"]
     rows = 4 * heads
     row_blocks = -(-rows // 16)
-    for ctx in [8192, 32768, 142000]:
-        S = lib.mla_decode_num_splits(1, 4, heads, ctx, 0, 256)
-        assert S * row_blocks >= sv["narrow_tile_workgroups"]
-        assert S * row_blocks >= 256
+    for cus in [80, 256, 304]:
+        for ctx in [16384, 32768, 142000]:
+            W = lib.mla_decode_num_splits(1, 4, heads, ctx, 0, cus)
+            assert cus - row_blocks < W * row_blocks <= cus
+            assert W * row_blocks > sv["wide_tile_workgroups"]
 
 
 @pytest.mark.parametrize("B,P,H,L", [(1, 1, 12, 1024), (32, 1, 12, 16384), (4, 4, 12, 32768),
-                                     (4, 4, 16, 32768), (8, 1, 12, 17750), (3, 2, 8, 64)])
-def test_planner_splits_are_whole_rounds_and_cover_the_range(lib, B, P, H, L):
+                                     (4, 4, 16, 32768), (8, 1, 12, 17750), (3, 2, 8, 64),
+                                     (1, 1, 12, 16), (0, 1, 12, 0)])
+def test_planner_pieces_fit_the_chip_and_the_work(lib, B, P, H, L):
+    """At most one work-group per CU, at least eight 16-token steps per piece (as far as
+    the max_kv_len hint tells), and as many pieces as both allow."""
+    RB = -(-(P * H) // 16)
     for cus in [80, 256, 304]:
-        S = lib.mla_decode_num_splits(B, P, H, L, 0, cus)
-        assert S >= 1
-        rounds = -(-L // 64)
-        assert S <= rounds
-        chunk_rounds = -(-rounds // S)
-        assert (S - 1) * chunk_rounds < rounds <= S * chunk_rounds
+        W = lib.mla_decode_num_splits(B, P, H, L, 0, cus)
+        steps = max(B, 1) * (-(-L // 16))
+        assert W == max(1, min(cus // RB, -(-steps // 8)))
+
+
+@pytest.mark.parametrize("B,P,H,L,S", [(32, 1, 12, 16384, 0), (4, 4, 12, 32768, 0),
+                                       (2, 3, 5, 100, 7), (1, 1, 12, 16, 0)])
+def test_workspace_holds_slots_and_counters(lib, B, P, H, L, S):
+    """A fixed block of 65536 counters first (the same bytes for every shape), then
+    (W + B) x rows partial outputs and lse, each part 256-byte aligned; nothing for a
+    single piece."""
+    W = lib.mla_decode_num_splits(B, P, H, L, S, 0)  # the plan the workspace query uses
+    R = P * H
+    al = lambda x: -(-x // 256) * 256
+    want = 0 if W <= 1 else 65536 * 4 + al((W + B) * R * 512 * 4) + al((W + B) * R * 4)
+    assert lib.mla_decode_workspace_size(B, P, H, L, S) == want
+
+
+def test_counter_capacity_is_enforced(lib):
+    """B x ceil(P*H/16) above the counter block's 65536 entries needs the single-piece
+    plan; any other piece count is rejected before the device is queried."""
+    assert lib.mla_verify(*verify_args(B=65537, H=12, splits=0)) == -2
+    assert lib.mla_verify(*verify_args(B=32769, H=17, splits=3)) == -2
+    assert lib.mla_verify(*verify_args(B=32768, H=17, splits=3, ws=None)) != -2
 
 
 def test_explicit_split_count_is_honoured(lib):

@@ -1,11 +1,12 @@
 """GPU parity of decode / verify / merge against the FP64 oracle, through the C-ABI.
 
 Small cases (the oracle computes every row) span several 16-token steps, several
-splits, ragged tails, partial last blocks, empty key ranges, 8 / 12 / 16 heads, one to
+pieces of the batch's step list, ragged tails, partial last blocks, empty key ranges, 8 / 12 / 16 heads, one to
 four query positions, BF16 and FP8 caches, FP32 and BF16 outputs.  The full-size
 workloads run in the launch configuration the bench times (automatic split plan) and
 are checked on every row (decode, 32 sequences) or on sampled rows (long contexts).
-Invariants: split count, head padding, paging layout, run-to-run determinism.
+Invariants: piece count, head padding, paging layout, run-to-run determinism, and the
+workspace contract (counters left zero).
 """
 import numpy as np
 import pytest
@@ -64,8 +65,10 @@ def test_small_parity(mla, kv_dtype, H, P):
     check_lse(lse, ref_l)
 
 
-@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 40])
+@pytest.mark.parametrize("num_splits", [1, 2, 3, 7, 40, 300])
 def test_explicit_split_counts(mla, num_splits):
+    """Pieces of the concatenated 16-token step list (152 steps here); 300 pieces is more
+    than there are steps, so only the first 152 take work."""
     q, cache = small_case(2001, [5, 333, 2047], 12, 2, "fp8")
     out, lse = run_gpu(mla, q, cache, num_splits=num_splits)
     ref_o, ref_l = run_oracle(q, cache)
@@ -111,6 +114,30 @@ def test_hint_smaller_than_the_range_still_covers_it(mla):
     ref_o, ref_l = run_oracle(q, cache)
     check_out(out, ref_o)
     check_lse(lse, ref_l)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("gain", [0.9, 2.0])
+def test_late_score_jump(mla, kv_dtype, gain):
+    """A key planted late in a sequence, parallel to one head's query: its score is about
+    gain * |q|^2 / sqrt(192) (~54 log2 units at gain 0.9, ~120 at gain 2), far above the
+    reference maximum the row started from.  Below the kernel's cap of 64 log2 units the
+    row keeps its reference and carries large probabilities; above it the wave runs its
+    steps again from the true maximum.  Both must match the oracle."""
+    lens = [900, 2500]
+    q, cache = small_case(2014, lens, 12, 1, kv_dtype)
+    qf = (q[1, 0, 5].astype(np.uint32) << 16).view(np.float32)
+    t = 2301  # late in sequence 1
+    blk = cache.block_table[1, t // cache.block_size]
+    if kv_dtype == "bf16":
+        cache.kv[blk, t % cache.block_size] = mi.to_bf16_bits(gain * qf)
+    else:
+        cache.kv[blk, t % cache.block_size] = mi.to_fp8_codes(gain * qf, cache.kv_scale)
+    out, lse = run_gpu(mla, q, cache, num_splits=3)
+    ref_o, ref_l = run_oracle(q, cache)
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+    assert ref_l[1, 0, 5] > ref_l[1, 0, 4] + 15  # the planted key dominates that row
 
 
 def test_merge_lse_matches_oracle(mla):
@@ -164,6 +191,28 @@ def test_paging_layout_is_bitwise_invariant(mla):
     assert torch.equal(a, c) and torch.equal(la, lc)
 
 
+def test_workspace_is_left_zero_and_serves_many_calls(mla):
+    """The workspace's completion counters start at zero and every call leaves them zero,
+    so one zero-filled workspace serves calls of different shapes in a row."""
+    ws = torch.zeros(64 << 20, dtype=torch.uint8, device=DEV)
+    cases = [(2010, [5, 333, 2047], 12, 2, "fp8", 7), (2011, [4000, 1, 900], 16, 4, "bf16", 0),
+             (2012, [64] * 9, 8, 1, "fp8", 5), (2013, [5, 333, 2047], 12, 2, "fp8", 7)]
+    for seed, lens, H, P, kvd, splits in cases:
+        q, cache = small_case(seed, lens, H, P, kvd)
+        kv, bt, sl = cache_to_device(cache, DEV)
+        B = len(lens)
+        need = mla.decode_workspace_size(B, P, H, max(lens), splits)
+        assert 0 < need <= ws.numel()
+        out, lse = mla.verify(bf16_tensor(q, DEV), kv, bt, sl, softmax_scale=SIGMA,
+                              kv_scale=cache.kv_scale, num_splits=splits, max_kv_len=max(lens),
+                              workspace=ws)
+        torch.cuda.synchronize()
+        ref_o, ref_l = run_oracle(q, cache)
+        check_out(out, ref_o)
+        check_lse(lse, ref_l)
+        assert torch.all(ws[:65536 * 4].view(torch.int32) == 0)
+
+
 def test_workspace_too_small_is_rejected(mla):
     q, cache = small_case(2009, [5000], 12, 1, "bf16")
     kv, bt, sl = cache_to_device(cache, DEV)
@@ -177,7 +226,7 @@ def test_workspace_too_small_is_rejected(mla):
 
 
 # ---------------------------------------------------------------------------
-# full-size workloads, automatic split plan (the bench's launch configuration)
+# full-size workloads, automatic piece plan (the bench's launch configuration)
 # ---------------------------------------------------------------------------
 
 def full_case(name):
