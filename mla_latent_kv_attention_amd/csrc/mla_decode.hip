@@ -50,21 +50,16 @@ constexpr int kWaves = 4;
 constexpr int kStep = 16;       // tokens per wave step
 constexpr int kKSteps = 18;     // 576 / 32
 constexpr int kVRow = 528;      // LDS row stride (bf16) of a wave's value tile (512 + 16 pad)
-constexpr int kQRow = kDK + 8;  // LDS row stride (bf16) of the query rows: 292 dwords, so the
-                                // 16 rows a fragment read touches start in 16 distinct banks
 constexpr int kORow = 516;      // LDS row stride (fp32) of the merged output tile
 constexpr float kCap = 64.0f;   // log2 units a score may exceed its row's reference max
 
 struct DecodeSmem {
-  uint16_t q[16 * kQRow];               // 18,688 B: the row block's queries
   union {
-    uint16_t v[kWaves][kStep * kVRow];  // 67,584 B: per-wave value tiles
+    uint16_t v[kWaves][2 * kStep * kVRow];  // 135,168 B: two value tiles per wave
     struct {
-      float o[16 * kORow];              // merged 16 x 512 accumulator
+      float o[kWaves][16 * kORow];          // 132,096 B: each wave's scaled accumulator
       float m[kWaves][16];
       float l[kWaves][16];
-      float row_m[16];
-      float row_l[16];
     } red;
   };
 };
@@ -302,20 +297,21 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     const int w_first = owner(rs, N, We), w_last = owner(rs + sr.n - 1, N, We);
 
     __syncthreads();  // the previous segment is done with the LDS tiles
-    // The row block's queries go to LDS once per segment (rows past R are zero);
-    // every step reads its Q^T fragments (B operand of the score MFMA) from there,
-    // three k-steps ahead of their MFMA, which keeps the 16 query rows out of the
-    // register budget.
-    for (int i = tid; i < 16 * (kDK / 8); i += 256) {
-      const int row = i / (kDK / 8), c8 = i % (kDK / 8);
-      const int rq = rb * 16 + row;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (rq < p.R) v = *(const u32x4*)(p.q + ((size_t)b * p.R + rq) * kDK + 8 * c8);
-      *(u32x4*)(sm.q + row * kQRow + 8 * c8) = v;
+    // The 18 Q^T fragments (B operand of the score MFMA) of the lane's query row stay
+    // in registers for the whole segment, loaded straight from global memory before
+    // the key prefetch: only MFMAs read them, so they can live in accumulation
+    // registers, and no score MFMA waits on an LDS read.  Rows past R are zero.
+    bf16x8 qreg[kKSteps];
+    {
+      const int rq = rb * 16 + col;
+      const uint16_t* qrow = p.q + ((size_t)b * p.R + min(rq, p.R - 1)) * kDK;
+  #pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        const bf16x8 v = *(const bf16x8*)(qrow + kdim(kk, grp));
+        qreg[kk] = rq < p.R ? v : (bf16x8){};
+      }
     }
-    __syncthreads();
-    const uint16_t* qsrc = sm.q + col * kQRow;
-    auto qfrag = [&](int kk) { return *(const bf16x8*)(qsrc + kdim(kk, grp)); };
+    auto qfrag = [&](int kk) { return qreg[kk]; };
 
     // Online softmax with a reference max that never moves inside the step loop.
     // A row's reference m_ref is its first visible score maximum (until then its
@@ -349,17 +345,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
         dst[i] = *(const u32x4*)(krow + (kFp8 ? 64 * i + 16 * grp : 2 * kdim(i, grp)));
     };
 
-    auto process_step = [&](const u32x4* raw, int t0) {
-      // scores: lane (col, grp) gets tokens t0 + 4 * grp + i of query row `col`; the value
-      // part of each fragment goes to this wave's LDS tile on the way (bf16, token-major).
-      // Schedule: the Q^T fragments of three k-steps are read before the first MFMA,
-      // then every MFMA is followed by the read of the fragment three steps later.
-      __builtin_amdgcn_sched_barrier(0);
+    // Score half of a step: the keys of step t0 (raw cache bytes) against the row
+    // block's queries.  Lane (col, grp) gets tokens t0 + 4 grp + i of query row col;
+    // the value part of each fragment goes to LDS tile `vt_w` on the way (bf16,
+    // token-major).  Returns P^T as the B operand of the value MFMA.
+    auto score_step = [&](const u32x4* raw, int t0, uint16_t* vt_w) -> i16x4 {
       f32x4 sc = {0.f, 0.f, 0.f, 0.f};
       // write bases: chunk 8 j + 2 grp + h of row col sits at chunk (8 j + 2 grp + (h ^ sw))
       const int sw = (col >> 3) & 1;
-      uint16_t* vrow0 = vt + col * kVRow + 16 * grp + 8 * sw;        // h = 0
-      uint16_t* vrow1 = vt + col * kVRow + 16 * grp + 8 * (sw ^ 1);  // h = 1
+      uint16_t* vrow0 = vt_w + col * kVRow + 16 * grp + 8 * sw;        // h = 0
+      uint16_t* vrow1 = vt_w + col * kVRow + 16 * grp + 8 * (sw ^ 1);  // h = 1
       if constexpr (kFp8) {
   #pragma unroll
         for (int j = 0; j < 9; ++j) {
@@ -380,18 +375,6 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
           sc = mfma_16x16x32(k, qfrag(kk), sc);
         }
       }
-
-      {
-        constexpr int kDsRead = 0x100, kMfma = 0x8, kAhead = 3;
-        __builtin_amdgcn_sched_group_barrier(kDsRead, kAhead, 0);
-  #pragma unroll
-        for (int i = 0; i < kKSteps - kAhead; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kMfma, kAhead, 0);
-      }
-
       float sv[4];
       float cm = -INFINITY;
   #pragma unroll
@@ -412,75 +395,91 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
         l_run += pv[i];
       }
       const bf16x4 pb = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
-      const i16x4 pf = __builtin_bit_cast(i16x4, pb);
-
-      wave_lds_fence();
-      // lane (col, grp) addresses token 4 grp + col / 4, dims 16 m + 4 (col % 4) .. + 3
-      const int vr = 4 * grp + (col >> 2);
-      const uint16_t* vsrc =
-          vt + vr * kVRow + 8 * (((col & 3) >> 1) ^ ((vr >> 3) & 1)) + 4 * (col & 1);
-  #pragma unroll
-      for (int m = 0; m < 32; ++m) acc[m] = mfma_16x16x16(lds_read_tr16(vsrc + 16 * m), pf, acc[m]);
-      {
-        // each transposed read runs four MFMAs ahead of its use: enough to cover the LDS
-        // latency without parking 32 fragments in registers
-        constexpr int kDsRead = 0x100, kMfma = 0x8, kAhead = 4;
-        __builtin_amdgcn_sched_group_barrier(kDsRead, kAhead, 0);
-  #pragma unroll
-        for (int i = 0; i < 32 - kAhead; ++i) {
-          __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
-        }
-        __builtin_amdgcn_sched_group_barrier(kMfma, kAhead, 0);
-      }
-      wave_lds_fence();
+      return __builtin_bit_cast(i16x4, pb);
     };
 
-    // A ring of kDepth register buffers per wave: the loads of the next kDepth - 1
-    // steps are in flight while a step computes (one step moves 9 KB of fp8 or
-    // 18 KB of bf16 rows per wave).  The loop is unrolled by kDepth so every buffer
+    // Value half of a step: O^T += V^T P^T from LDS tile `vt_r`, read transposed.
+    // Lane (col, grp) addresses token 4 grp + col / 4, dims 16 m + 4 (col % 4) .. + 3.
+    const int vr = 4 * grp + (col >> 2);
+    const int v_lane = vr * kVRow + 8 * (((col & 3) >> 1) ^ ((vr >> 3) & 1)) + 4 * (col & 1);
+    auto pv_step = [&](const uint16_t* vt_r, i16x4 pf) {
+      const uint16_t* vsrc = vt_r + v_lane;
+      // The transposed reads run kAheadV MFMAs ahead (16 for fp8 caches, 8 for bf16,
+      // whose larger register ring leaves less room), so the LDS latency is paid
+      // about once per step rather than once per MFMA.
+      constexpr int kAheadV = kFp8 ? 32 : 8;
+      i16x4 vf[32];
+  #pragma unroll
+      for (int m = 0; m < 32; ++m) vf[m] = lds_read_tr16(vsrc + 16 * m);
+  #pragma unroll
+      for (int m = 0; m < 32; ++m) acc[m] = mfma_16x16x16(vf[m], pf, acc[m]);
+      constexpr int kDsRead = 0x100, kMfma = 0x8;
+      __builtin_amdgcn_sched_group_barrier(kDsRead, kAheadV, 0);
+  #pragma unroll
+      for (int m = 0; m < 32 - kAheadV; ++m) {
+        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kMfma, kAheadV, 0);
+    };
+
+    // The two halves are software-pipelined: while the value MFMAs of step i run,
+    // the same wave widens, stores and scores step i + 1 (two LDS value tiles per
+    // wave alternate), so the matrix pipe is not idle through the conversion,
+    // softmax and LDS round trips of one step.  A ring of kDepth register buffers
+    // keeps the loads of the next steps in flight (one step moves 9 KB of fp8 or
+    // 18 KB of bf16 rows per wave); the loop is unrolled by kDepth so every buffer
     // index is a compile-time constant.
     constexpr int kDepth = kFp8 ? 3 : 2;
     constexpr int kStride = kStep * kWaves;
     const int t_first = sr.base + kStep * (a + wave);
     const int n_steps = a + wave < e ? (e - a - wave + kWaves - 1) / kWaves : 0;
-    // Every step issues the same loads (prefetches past the wave's last step re-read
-    // that step), and the steady-state loop below has no branch around them, so the
-    // compiler counts them exactly and keeps the whole ring in flight.
+    // Every iteration issues the same loads (prefetches past the wave's last step
+    // re-read that step), so the compiler counts them exactly and keeps the whole
+    // ring in flight.
     u32x4 ring[kDepth][kLoads];
     const int last_t0 = t_first + (n_steps - 1) * kStride;
     auto step_t0 = [&](int i) { return min(t_first + i * kStride, last_t0); };
+    auto tile = [&](int i) { return vt + (i & 1) * (kStep * kVRow); };
     for (int pass = 0; pass < 2; ++pass) {
   #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
-    long row_next = 0;  // cache row of the step the next prefetch loads (read a step early)
     if (n_steps > 0) {
+      long row_next;  // cache row of the step the next prefetch loads (read a step early)
   #pragma unroll
-      for (int u = 0; u < kDepth - 1; ++u) load_step(step_row(step_t0(u)), step_t0(u), ring[u]);
-      row_next = step_row(step_t0(kDepth - 1));
-    }
-    int i0 = 0;
-    for (; i0 + kDepth <= n_steps; i0 += kDepth) {
-  #pragma unroll
-      for (int u = 0; u < kDepth; ++u) {
-        const int i = i0 + u;
-        load_step(row_next, step_t0(i + kDepth - 1), ring[(u + kDepth - 1) % kDepth]);
-        row_next = step_row(step_t0(i + kDepth));
+      for (int u = 0; u < kDepth; ++u) load_step(step_row(step_t0(u)), step_t0(u), ring[u]);
+      row_next = step_row(step_t0(kDepth));
+      i16x4 pf = score_step(ring[0], t_first, tile(0));
+      wave_lds_fence();
+      // iteration i: prefetch step i + kDepth into the slot step i left, score step
+      // i + 1, accumulate step i
+      auto body = [&](int i, const u32x4* raw_next, u32x4* slot_free) {
+        load_step(row_next, step_t0(i + kDepth), slot_free);
+        row_next = step_row(step_t0(i + kDepth + 1));
         __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the step computes
-        process_step(ring[u], t_first + i * kStride);
-      }
-    }
-    // tail: fewer than kDepth steps remain and all of them are already loaded
+        const i16x4 pf_next = score_step(raw_next, t_first + (i + 1) * kStride, tile(i + 1));
+        pv_step(tile(i), pf);
+        pf = pf_next;
+        wave_lds_fence();
+      };
+      int i0 = 0;
+      for (; i0 + kDepth < n_steps; i0 += kDepth) {
   #pragma unroll
-    for (int u = 0; u < kDepth - 1; ++u)
-      if (i0 + u < n_steps) process_step(ring[u], t_first + (i0 + u) * kStride);
+        for (int u = 0; u < kDepth; ++u) body(i0 + u, ring[(u + 1) % kDepth], ring[u]);
+      }
+  #pragma unroll
+      for (int u = 0; u < kDepth - 1; ++u)
+        if (i0 + u + 1 < n_steps) body(i0 + u, ring[(u + 1) % kDepth], ring[u]);
+      pv_step(tile(n_steps - 1), pf);
+      wave_lds_fence();
+    }
     // a row beyond its cap: run the steps again from its true maximum
     if (!__builtin_amdgcn_ballot_w64(m_max > m_ref + kCap)) break;
     m_ref = m_max;
     }
 
-    // ---- merge the four waves ----
+    // ---- merge the four waves: one round through LDS ----
     const float l_row = wave_sum16x4(l_run);
     __syncthreads();  // value tiles are dead from here on; the union is reused
     if (grp == 0) {
@@ -488,50 +487,47 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
       sm.red.l[wave][col] = l_row;
     }
     __syncthreads();
-    float M = -INFINITY;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm.red.m[v][col]);
-    float Lsum = 0.f;
-#pragma unroll
-    for (int v = 0; v < kWaves; ++v) {
-      const float mv = sm.red.m[v][col];
-      if (mv != -INFINITY) Lsum += sm.red.l[v][col] * fast_exp2(mv - M);
+    {
+      float M = -INFINITY;
+  #pragma unroll
+      for (int v = 0; v < kWaves; ++v) M = fmaxf(M, sm.red.m[v][col]);
+      const float my_scale = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - M);
+      // acc[m][i] = O[row col][dim 16 m + 4 grp + i]
+      float* orow = sm.red.o[wave] + col * kORow + 4 * grp;
+  #pragma unroll
+      for (int m = 0; m < 32; ++m) *(f32x4*)(orow + 16 * m) = acc[m] * my_scale;
     }
-    const float my_scale = (m_ref == -INFINITY) ? 0.f : fast_exp2(m_ref - M);
-    if (wave == 0 && grp == 0) {
-      sm.red.row_m[col] = M;
-      sm.red.row_l[col] = Lsum;
-    }
-    // acc[m][i] = O[row col][dim 16 m + 4 grp + i]
-    float* orow = sm.red.o + col * kORow + 4 * grp;
-    for (int v = 0; v < kWaves; ++v) {
-      if (wave == v) {
-#pragma unroll
-        for (int m = 0; m < 32; ++m) {
-          f32x4 x = acc[m] * my_scale;
-          if (v > 0) x += *(const f32x4*)(orow + 16 * m);
-          *(f32x4*)(orow + 16 * m) = x;
-        }
-      }
-      __syncthreads();
-    }
+    __syncthreads();
 
     // ---- this piece's result for sequence b: final rows, or a partial + merge ----
     const int orow_i = tid >> 4;  // 16 threads per output row
     const int rr = rb * 16 + orow_i;
     const bool rr_ok = rr < p.R;
-    const float Mr = sm.red.row_m[orow_i];
-    const float Lr = sm.red.row_l[orow_i];
+    float Mr = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) Mr = fmaxf(Mr, sm.red.m[v][orow_i]);
+    float Lr = 0.f;
+#pragma unroll
+    for (int v = 0; v < kWaves; ++v) {
+      const float mv = sm.red.m[v][orow_i];
+      if (mv != -INFINITY) Lr += sm.red.l[v][orow_i] * fast_exp2(mv - Mr);
+    }
     const float inv = (Lr > 0.f) ? p.out_scale / Lr : 0.f;
     const float lse_v = (Lr > 0.f) ? (Mr + fast_log2(Lr)) * kLn2 : -INFINITY;
     const size_t n = (size_t)b * p.R + rr;
-    const float* src = sm.red.o + orow_i * kORow;
+    // the four waves' scaled rows summed: dims d .. d + 3 of output row orow_i
+    auto merged = [&](int d) {
+      f32x4 x = *(const f32x4*)(sm.red.o[0] + orow_i * kORow + d);
+  #pragma unroll
+      for (int v = 1; v < kWaves; ++v) x += *(const f32x4*)(sm.red.o[v] + orow_i * kORow + d);
+      return x;
+    };
     if (w_first == w_last) {  // this piece holds the whole sequence
       if (rr_ok) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int d = 4 * (tid & 15) + 64 * k;
-          store_row4(p, n, d, *(const f32x4*)(src + d) * inv);
+          store_row4(p, n, d, merged(d) * inv);
         }
         if (p.lse && (tid & 15) == 0) p.lse[n] = lse_v;
       }
@@ -545,7 +541,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const int d = 4 * (tid & 15) + 64 * k;
-          store_agent16(rsrc, (uint32_t)(rr * kDV + d) * 4, *(const f32x4*)(src + d) * inv);
+          store_agent16(rsrc, (uint32_t)(rr * kDV + d) * 4, merged(d) * inv);
         }
       }
     }
