@@ -87,6 +87,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (the reference kernel "
+                         "for scaling HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -95,6 +98,15 @@ def main():
         sys.exit(2)
 
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "dispatches": 5}), flush=True)
+        return
     import mla_inputs as mi
     import mla_latent_kv_attention_amd as mla
     from mla_latent_kv_attention_amd import accounting as acc
