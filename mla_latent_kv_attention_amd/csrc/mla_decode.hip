@@ -60,6 +60,7 @@ struct DecodeSmem {
       float o[kWaves][16 * kORow];          // 132,096 B: each wave's scaled accumulator
       float m[kWaves][16];
       float l[kWaves][16];
+      float lb[kWaves][16];
     } red;
   };
 };
@@ -318,14 +319,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     // accumulator is zero, so setting it needs no rescale); later scores enter as
     // 2^(s - m_ref), which bf16 and fp32 hold exactly in range up to 2^kCap.  The
     // exponent is capped there, and m_max tracks the true maximum: a wave in which
-    // some row went more than kCap above its reference runs its steps again with
-    // the true maximum as reference (no score can exceed it then).  Keeping the
+    // some row went more than kCap above its reference runs its steps again, those
+    // rows from their true maximum (no score can exceed it then), the others from
+    // the same reference as before, so they come out bit-identical.  Keeping the
     // accumulator free of a data-dependent rescale keeps it in place in the
     // accumulation registers for the whole loop.
     f32x4 acc[32];
     float m_ref = -INFINITY;
     float m_max = -INFINITY;
-    float l_run = 0.f;
+    float l_run = 0.f;   // sum of the fp32 probabilities: the lse
+    float lb_run = 0.f;  // sum of their bf16 roundings: the output's normaliser
 
     // Cache row of token t0 of an aligned step.  t0 is uniform, so the block id comes
     // through the scalar cache and stays out of the vector-load queue: a vector load
@@ -394,7 +397,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
         pv[i] = fast_exp2(fminf(sv[i] - mref, kCap));
         l_run += pv[i];
       }
+      // The value MFMA weighs the keys with P rounded to bf16; the output is
+      // normalised by the sum of those same rounded weights (lb_run), so it is an
+      // exact convex combination of the values it used and a key that dominates its
+      // row contributes its value unchanged; lse keeps the exact fp32 sum l_run.
       const bf16x4 pb = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) lb_run += (float)pb[i];
       return __builtin_bit_cast(i16x4, pb);
     };
 
@@ -404,8 +413,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     const int v_lane = vr * kVRow + 8 * (((col & 3) >> 1) ^ ((vr >> 3) & 1)) + 4 * (col & 1);
     auto pv_step = [&](const uint16_t* vt_r, i16x4 pf) {
       const uint16_t* vsrc = vt_r + v_lane;
-      // The transposed reads run kAheadV MFMAs ahead (16 for fp8 caches, 8 for bf16,
-      // whose larger register ring leaves less room), so the LDS latency is paid
+      // The transposed reads run kAheadV MFMAs ahead (all 32 for fp8 caches, 8 for
+      // bf16, whose larger register ring leaves less room), so the LDS latency is paid
       // about once per step rather than once per MFMA.
       constexpr int kAheadV = kFp8 ? 32 : 8;
       i16x4 vf[32];
@@ -445,6 +454,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
   #pragma unroll
     for (int i = 0; i < 32; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
     l_run = 0.f;
+    lb_run = 0.f;
     if (n_steps > 0) {
       long row_next;  // cache row of the step the next prefetch loads (read a step early)
   #pragma unroll
@@ -476,15 +486,18 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     }
     // a row beyond its cap: run the steps again from its true maximum
     if (!__builtin_amdgcn_ballot_w64(m_max > m_ref + kCap)) break;
-    m_ref = m_max;
+    // only the rows that went past their cap move; the others recompute bit-identically
+    m_ref = (m_max > m_ref + kCap) ? m_max : m_ref;
     }
 
     // ---- merge the four waves: one round through LDS ----
     const float l_row = wave_sum16x4(l_run);
+    const float lb_row = wave_sum16x4(lb_run);
     __syncthreads();  // value tiles are dead from here on; the union is reused
     if (grp == 0) {
       sm.red.m[wave][col] = m_ref;
       sm.red.l[wave][col] = l_row;
+      sm.red.lb[wave][col] = lb_row;
     }
     __syncthreads();
     {
@@ -506,13 +519,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     float Mr = -INFINITY;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) Mr = fmaxf(Mr, sm.red.m[v][orow_i]);
-    float Lr = 0.f;
+    float Lr = 0.f, Lb = 0.f;
 #pragma unroll
     for (int v = 0; v < kWaves; ++v) {
       const float mv = sm.red.m[v][orow_i];
-      if (mv != -INFINITY) Lr += sm.red.l[v][orow_i] * fast_exp2(mv - Mr);
+      if (mv != -INFINITY) {
+        const float sc = fast_exp2(mv - Mr);
+        Lr += sm.red.l[v][orow_i] * sc;
+        Lb += sm.red.lb[v][orow_i] * sc;
+      }
     }
-    const float inv = (Lr > 0.f) ? p.out_scale / Lr : 0.f;
+    const float inv = (Lb > 0.f) ? p.out_scale / Lb : 0.f;
     const float lse_v = (Lr > 0.f) ? (Mr + fast_log2(Lr)) * kLn2 : -INFINITY;
     const size_t n = (size_t)b * p.R + rr;
     // the four waves' scaled rows summed: dims d .. d + 3 of output row orow_i

@@ -15,7 +15,7 @@
 // widened exactly on the way in) with the next tile's loads in flight, and
 // read by all four waves:
 //   S^T[32 tokens x 32 rows] = K Q^T           36 MFMA 32x32x16 (A from LDS)
-//   causal mask, online softmax (running max moved only when it trails by > 2^8)
+//   causal mask, online softmax against a per-row reference fixed in the first tile
 //   O^T[512 x 32 rows] += V^T P^T               32 MFMA 32x32x16 (A = V^T read
 //                                               with ds_read_b64_tr_b16, B = P^T
 //                                               straight from the score registers)
@@ -43,7 +43,7 @@ constexpr int kTileElems = kTile * kPRow;
 constexpr int kDmaPerWave = 10;                  // 4 waves x 10 x 1 KB cover a padded tile
 constexpr int kSlotBytes = 4 * kDmaPerWave * 1024;
 constexpr int kRing = 3;                         // bf16 tiles in flight / in use
-constexpr float kSlack = 8.0f;
+constexpr float kCap = 64.0f;  // log2 units a score may exceed its row's reference max
 
 static_assert(kTile * kPRowChunks <= 4 * kDmaPerWave * 64, "DMA slots must cover a tile");
 
@@ -146,23 +146,6 @@ struct Fp8Stage {
   }
 };
 
-// acc *= s for a 16-register MFMA accumulator kept in AGPRs: each element is read
-// into a VGPR, scaled and written back, so the accumulator keeps its register
-// class across the key loop (a plain multiply would move all 256 accumulator
-// values through VGPRs on every iteration).
-__device__ __forceinline__ void scale_acc(f32x16& acc, float s) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    float x = acc[i];
-    float t;
-    asm volatile(
-        "v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %2, %1\n\tv_accvgpr_write_b32 %0, %1"
-        : "+a"(x), "=&v"(t)
-        : "v"(s));
-    acc[i] = x;
-  }
-}
-
 template <bool kFp8>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) {
   // bf16: a ring of 3 DMA slots (120 KB); fp8: two register-staged tiles (73 KB)
@@ -209,11 +192,19 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   // their first use inside the key loop would also drain the tile copies in flight
   wait_vmcnt<0>();
 
+  // Online softmax with a reference max that never moves inside the key loop: a
+  // row's reference is its maximum over the first tile (key 0, visible to every
+  // row, is in it); later scores enter as 2^(s - m_ref), exact in bf16 and fp32 up
+  // to 2^kCap, where the exponent is capped while m_max tracks the true maximum.
+  // If any row of the work-group went more than kCap above its reference, the
+  // whole work-group runs the key loop again, those rows from their true maxima and
+  // the others from unchanged references (bit-identical results).  With no
+  // data-dependent rescale the accumulator stays in its registers for the loop.
   f32x16 acc[16];
-#pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = (f32x16){};
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_ref = -INFINITY;
+  float m_max = -INFINITY;
+  float l_run = 0.f;   // sum of the fp32 probabilities: the lse
+  float lb_run = 0.f;  // sum of their bf16 roundings: the output's normaliser
 
   // per-lane LDS offsets (elements) inside a tile
   const int a_off = n * kPRow + 8 * g;  // K fragment: token n, dims 16 kk + 8 g
@@ -243,30 +234,29 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
         cm = fmaxf(cm, sv[i]);
       }
       cm = fmaxf(cm, __shfl_xor(cm, 32));
-      const float mn = fmaxf(m_run, cm);
-      const bool need = mn > m_run + kSlack;
-      if (__builtin_amdgcn_ballot_w64(need)) {
-        const float alpha = need ? fast_exp2(m_run - mn) : 1.f;
-        if (need) m_run = mn;
-        l_run *= alpha;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) scale_acc(acc[i], alpha);
-      }
-      const float mref = (m_run == -INFINITY) ? 0.f : m_run;
+      m_max = fmaxf(m_max, cm);
+      m_ref = (m_ref == -INFINITY) ? cm : m_ref;
+      const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
       float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pv[i] = fast_exp2(sv[i] - mref);
+        pv[i] = fast_exp2(fminf(sv[i] - mref, kCap));
         l_run += pv[i];
       }
       // k-slot 8 g + s of k-step j holds token 16 j + 8 (s / 4) + 4 g + s % 4: exactly
       // the score values i = 8 j + s this lane already has
+      // the value MFMA weighs the keys with P rounded to bf16, and the output is
+      // normalised by the sum of those same weights (an exact convex combination of
+      // the values: a key that dominates its row contributes its value unchanged)
       bf16x8 pf[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        pf[j] = (bf16x8){(__bf16)pv[8 * j + 0], (__bf16)pv[8 * j + 1], (__bf16)pv[8 * j + 2],
-                         (__bf16)pv[8 * j + 3], (__bf16)pv[8 * j + 4], (__bf16)pv[8 * j + 5],
-                         (__bf16)pv[8 * j + 6], (__bf16)pv[8 * j + 7]};
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          pf[j][i] = (__bf16)pv[8 * j + i];
+          lb_run += (float)pf[j][i];
+        }
+      }
 #pragma unroll
       for (int mb = 0; mb < 16; ++mb) {
 #pragma unroll
@@ -282,6 +272,11 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
     }
   };
 
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) acc[i] = (f32x16){};
+  l_run = 0.f;
+  lb_run = 0.f;
   if constexpr (kFp8) {
     Fp8Stage st;
     st.load(p.kv, seq_start, len, 0, tid);
@@ -312,14 +307,20 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
       compute(lds + (kt % kRing) * (kSlotBytes / 2), kt);
     }
   }
+  // a row beyond its cap anywhere in the work-group: all waves run the loop again
+  if (!__syncthreads_or(m_max > m_ref + kCap)) break;
+  // only the rows that went past their cap move; the others recompute bit-identically
+  m_ref = (m_max > m_ref + kCap) ? m_max : m_ref;
+  }
 
   // ---- finalize this lane's row
   const float l_row = l_run + __shfl_xor(l_run, 32);
+  const float lb_row = lb_run + __shfl_xor(lb_run, 32);
   if (!row_ok) return;
-  const float inv = (l_row > 0.f) ? p.out_scale / l_row : 0.f;
+  const float inv = (lb_row > 0.f) ? p.out_scale / lb_row : 0.f;
   const size_t orow = (size_t)seq_start * p.H + r;
   if (p.lse && g == 0)
-    p.lse[orow] = (l_row > 0.f) ? (m_run + fast_log2(l_row)) * kLn2 : -INFINITY;
+    p.lse[orow] = (l_row > 0.f) ? (m_ref + fast_log2(l_row)) * kLn2 : -INFINITY;
   // acc[mb][i]: dim 32 mb + 8 (i / 4) + 4 g + i % 4
 #pragma unroll
   for (int mb = 0; mb < 16; ++mb) {

@@ -109,6 +109,28 @@ def test_future_keys_do_not_matter_and_runs_repeat(mla):
     assert torch.equal(a[:150], b[:150]) and torch.equal(la[:150], lb[:150])
 
 
+@pytest.mark.parametrize("gain", [0.9, 2.0])
+def test_late_score_jump(mla, gain):
+    """A key planted at token 300 parallel to the query of token 350, head 4: its score is
+    ~54 (gain 0.9) or ~120 (gain 2) log2 units above the first tile's maximum of that row,
+    below and above the kernel's cap of 64.  Above the cap the work-group runs its key loop
+    again; rows that stayed under their cap (every row before token 300 in particular) must
+    come out bit-identical to a run without the planted key, and every row must match the
+    oracle."""
+    T, H = 400, 12
+    d = mi.prefill_inputs(mi.PrefillWorkload("small", [T], H, "bf16", seed=3105))
+    base, lbase = run_gpu(mla, d, "bf16")
+    d2 = dict(d)
+    d2["kv"] = d["kv"].copy()
+    qf = (d["q"][350, 4].astype(np.uint32) << 16).view(np.float32)
+    d2["kv"][300] = mi.to_bf16_bits(gain * qf)
+    out, lse = run_gpu(mla, d2, "bf16")
+    ref_o, ref_l = run_oracle(d2, "bf16")
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+    assert torch.equal(out[:300], base[:300]) and torch.equal(lse[:300], lbase[:300])
+
+
 def test_max_seqlen_hint_does_not_limit_the_work(mla):
     d = mi.prefill_inputs(mi.PrefillWorkload("small", [200, 90], 12, "fp8", seed=3104))
     out, lse = run_gpu(mla, d, "fp8", max_seqlen=8)
