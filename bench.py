@@ -77,6 +77,52 @@ def cpu_baseline(q, cache, alg_bytes, min_seconds=10.0, max_reps=400):
                       "oracle time on %d threads" % (DECODE_WORKLOAD, reps, el, threads)}
 
 
+def run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
+                stream, result):
+    """Causal prefill of the 32K x 12-head workload: parity on sampled tokens, then timing."""
+    pw = mi.WORKLOADS[PREFILL_WORKLOAD]
+    log("generating", pw.name)
+    pd = mi.prefill_inputs(pw)
+    T = pw.total_tokens
+    pq = bf16_tensor(pd["q"], dev).reshape(T, pw.heads, 576)
+    pkv = bf16_tensor(pd["kv"], dev).reshape(T, 576)
+    cu = torch.from_numpy(pd["cu_seqlens"]).to(dev)
+    pout = torch.empty((T, pw.heads, 512), dtype=torch.bfloat16, device=dev)
+    plse = torch.empty((T, pw.heads), dtype=torch.float32, device=dev)
+
+    def pstep():
+        mla.prefill(pq, pkv, cu, softmax_scale=pw.softmax_scale, max_seqlen=T,
+                    out_dtype=torch.bfloat16, out=pout, lse=plse)
+    pstep()
+    torch.cuda.synchronize()
+    toks = np.array([0, 1, 4095, T - 1], np.int64)
+    ro, rl = oracle.prefill(pd["q"], pd["kv"], False, 1.0, pd["cu_seqlens"],
+                            pw.softmax_scale, tokens=toks)
+    ti = torch.from_numpy(toks).to(dev)
+    check_out(pout[ti], ro, "prefill out")
+    check_lse(plse[ti], rl, "prefill lse")
+    pstep()
+    pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.prefill_steps)]
+    torch.cuda.synchronize()
+    for a, b in pe:
+        a.record(stream)
+        pstep()
+        b.record(stream)
+    torch.cuda.synchronize()
+    pms = np.array([a.elapsed_time(b) for a, b in pe])
+    pflops = acc.prefill_flops(pw.seq_lens, pw.heads)
+    tflops = pflops / (pms.mean() * 1e-3) / 1e12
+    result["prefill"] = {
+        "workload": PREFILL_WORKLOAD, "tokens_per_s": round(T / (pms.mean() * 1e-3), 1),
+        "ms": round(float(pms.mean()), 3), "tflops": round(tflops, 1),
+        "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+        "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": pflops,
+        "kernel": "prefill_kernel<bf16>"}
+    log("prefill: %.2f ms, %.0f tok/s, %.1f TFLOP/s" % (pms.mean(), T / (pms.mean() * 1e-3),
+                                                      tflops))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -86,6 +132,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0, help="pieces; 0 = automatic plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="prefill figures only (for profiling the prefill kernel)")
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (the reference kernel "
@@ -117,6 +165,17 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream(dev)
+
+    if args.no_decode:
+        result = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "steps": 0,
+                  "warmup": 0, "ms_per_step": None, "higher_is_better": True,
+                  "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+                  "data": "synthetic", "config": {"workload": PREFILL_WORKLOAD}}
+        import oracle
+        run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
+                    stream, result)
+        print(json.dumps(result), flush=True)
+        return
 
     # ---------------- decode workload ----------------
     w = mi.WORKLOADS[DECODE_WORKLOAD]
@@ -208,47 +267,8 @@ def main():
 
     # ---------------- prefill (the metric's second half) ----------------
     if not args.no_prefill:
-        pw = mi.WORKLOADS[PREFILL_WORKLOAD]
-        log("generating", pw.name)
-        pd = mi.prefill_inputs(pw)
-        T = pw.total_tokens
-        pq = bf16_tensor(pd["q"], dev).reshape(T, pw.heads, 576)
-        pkv = bf16_tensor(pd["kv"], dev).reshape(T, 576)
-        cu = torch.from_numpy(pd["cu_seqlens"]).to(dev)
-        pout = torch.empty((T, pw.heads, 512), dtype=torch.bfloat16, device=dev)
-        plse = torch.empty((T, pw.heads), dtype=torch.float32, device=dev)
-
-        def pstep():
-            mla.prefill(pq, pkv, cu, softmax_scale=pw.softmax_scale, max_seqlen=T,
-                        out_dtype=torch.bfloat16, out=pout, lse=plse)
-        pstep()
-        torch.cuda.synchronize()
-        toks = np.array([0, 1, 4095, T - 1], np.int64)
-        ro, rl = oracle.prefill(pd["q"], pd["kv"], False, 1.0, pd["cu_seqlens"],
-                                pw.softmax_scale, tokens=toks)
-        ti = torch.from_numpy(toks).to(dev)
-        check_out(pout[ti], ro, "prefill out")
-        check_lse(plse[ti], rl, "prefill lse")
-        pstep()
-        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.prefill_steps)]
-        torch.cuda.synchronize()
-        for a, b in pe:
-            a.record(stream)
-            pstep()
-            b.record(stream)
-        torch.cuda.synchronize()
-        pms = np.array([a.elapsed_time(b) for a, b in pe])
-        pflops = acc.prefill_flops(pw.seq_lens, pw.heads)
-        tflops = pflops / (pms.mean() * 1e-3) / 1e12
-        result["prefill"] = {
-            "workload": PREFILL_WORKLOAD, "tokens_per_s": round(T / (pms.mean() * 1e-3), 1),
-            "ms": round(float(pms.mean()), 3), "tflops": round(tflops, 1),
-            "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-            "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": pflops,
-            "kernel": "prefill_kernel<bf16>"}
-        log("prefill: %.2f ms, %.0f tok/s, %.1f TFLOP/s" % (pms.mean(), T / (pms.mean() * 1e-3),
-                                                          tflops))
+        run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
+                    stream, result)
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
