@@ -77,6 +77,164 @@ def cpu_baseline(q, cache, alg_bytes, min_seconds=10.0, max_reps=400):
                       "oracle time on %d threads" % (DECODE_WORKLOAD, reps, el, threads)}
 
 
+def gpu_clocks():
+    """Current shader / memory clocks as the SMI tool reports them (text), or None."""
+    import subprocess
+    for cmd in (["amd-smi", "metric", "--clock"], ["rocm-smi", "--showclocks"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            lines = [l.strip() for l in r.stdout.splitlines()
+                     if any(k in l.upper() for k in ("SCLK", "MCLK", "GFX_0", "MEM_0", "CLK"))]
+            return " | ".join(lines[:12]) or None
+    return None
+
+
+def event_times(torch, stream, fn, n):
+    """HIP-event duration (ms) of each of n calls of fn on `stream`."""
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        a.record(stream)
+        fn(i)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in ev])
+
+
+def graph_replay_us(torch, fns, out, calls=100, replays=5):
+    """Capture `calls` launches (cycling through fns) into one HIP graph; check that
+    every replay reproduces the eager result bitwise (eager work and a synchronisation
+    between replays), then time replays.  Returns microseconds per call."""
+    fns[0]()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fns[i % len(fns)]()
+    for _ in range(3):
+        out.zero_()
+        fns[0]()                       # eager work between replays
+        torch.cuda.synchronize()
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref):
+            raise AssertionError("graph replay differs from the eager call")
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    a.record(s)
+    for _ in range(replays):
+        g.replay()
+    b.record(s)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) * 1e3 / (replays * calls)
+
+
+def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device, check_out,
+                      check_lse, dev, stream):
+    """The other decode / verify configurations: parity on sampled rows, then per-call
+    HIP-event times (p10 / p50 / p90) and, for the launch-bound ones, HIP-graph replays."""
+    res = {}
+    for name, rotate in (("decode_b1_h12_l1024_bf16", 1), ("verify_b4_p4_h12_l32768_bf16", 4)):
+        w = mi.WORKLOADS[name]
+        log("generating", name)
+        d = mi.decode_inputs(w)
+        q_np, cache = d["q"], d["cache"]
+        B, P, H = q_np.shape[:3]
+        L = [int(x) for x in cache.seq_lens]
+        kv0, bt, sl = cache_to_device(cache, dev)
+        pools = [kv0] + [kv0.clone() for _ in range(rotate - 1)]
+        q = bf16_tensor(q_np, dev).reshape(B, P, H, 576)
+        out = torch.empty((B, P, H, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, P, H), dtype=torch.float32, device=dev)
+        ws = torch.zeros(max(1, mla.decode_workspace_size(B, P, H, max(L))), dtype=torch.uint8,
+                         device=dev)
+        fns = [mla.verify_launcher(q, kv, bt, sl, softmax_scale=w.softmax_scale,
+                                   kv_scale=cache.kv_scale, max_kv_len=max(L), out=out, lse=lse,
+                                   workspace=ws) for kv in pools]
+        N = B * P * H
+        rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(9).choice(
+            N, min(N, 24), replace=False)])).astype(np.int64)
+        ro, rl = oracle.decode(q_np, cache.kv, cache.kv_dtype == "fp8", cache.kv_scale,
+                               cache.block_table, cache.seq_lens, w.softmax_scale, rows=rows)
+        for f in fns:
+            f()
+            torch.cuda.synchronize()
+            idx = torch.from_numpy(rows).to(dev)
+            check_out(out.reshape(N, 512)[idx], ro, name + " out")
+            check_lse(lse.reshape(N)[idx], rl, name + " lse")
+        ms = event_times(torch, stream, lambda i: fns[i % len(fns)](), 100)
+        ab = acc.decode_bytes(L, P, H, w.kv_dtype, out_bytes=4, block_size=cache.block_size)
+        us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
+        g_us = graph_replay_us(torch, fns, out)
+        res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us],
+                     "graph_replay_us": round(g_us, 2), "algorithmic_bytes": ab,
+                     "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
+                     "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4),
+                     "pieces": mla.decode_num_splits(B, P, H, max(L)), "kv_pool_copies": rotate}
+        log("%s: p50 %.1f us (graph %.1f us), %.0f GB/s" % (name, us[1], g_us,
+                                                          res[name]["gbs_p50"]))
+        del pools, kv0, fns
+
+    # 142,000-token contexts in 8 contiguous partitions (one call each, as a position shard
+    # would compute its share) merged by mla_merge_lse
+    name = "decode_b8_h12_l142000_fp8_8parts"
+    w = mi.WORKLOADS[name]
+    log("generating", name)
+    d = mi.decode_inputs(w)
+    q_np, cache = d["q"], d["cache"]
+    B, P, H = q_np.shape[:3]
+    N = B * P * H
+    kv, bt, sl = cache_to_device(cache, dev)
+    q = bf16_tensor(q_np, dev).reshape(B, P, H, 576)
+    bounds = mi.partition_bounds(int(cache.seq_lens[0]), w.partitions)
+    S = len(bounds)
+    part_out = torch.empty((S, B, P, H, 512), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((S, B, P, H), dtype=torch.float32, device=dev)
+    out = torch.empty((N, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((N,), dtype=torch.float32, device=dev)
+    span = max(hi - lo for lo, hi in bounds)
+    wss = [torch.zeros(max(1, mla.decode_workspace_size(B, P, H, span)), dtype=torch.uint8,
+                       device=dev) for _ in bounds]
+    kbs = [torch.full((B,), lo, dtype=torch.int32, device=dev) for lo, _ in bounds]
+    kes = [torch.full((B,), hi, dtype=torch.int32, device=dev) for _, hi in bounds]
+    fns = [mla.verify_launcher(q, kv, bt, sl, softmax_scale=w.softmax_scale,
+                               kv_scale=cache.kv_scale, max_kv_len=span, out=part_out[j],
+                               lse=part_lse[j], workspace=wss[j], kv_begin=kbs[j], kv_end=kes[j])
+           for j in range(S)]
+
+    def call(_):
+        for f in fns:
+            f()
+        mla.merge_lse(part_out.reshape(S, N, 512), part_lse.reshape(S, N), out=out, lse=lse)
+    call(0)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(10).choice(
+        N, 16, replace=False)])).astype(np.int64)
+    ro, rl = oracle.decode(q_np, cache.kv, True, cache.kv_scale, cache.block_table,
+                           cache.seq_lens, w.softmax_scale, rows=rows)
+    idx = torch.from_numpy(rows).to(dev)
+    check_out(out[idx], ro, name + " out")
+    check_lse(lse[idx], rl, name + " lse")
+    ms = event_times(torch, stream, call, 30)
+    L = [int(x) for x in cache.seq_lens]
+    ab = sum(acc.decode_bytes(L, P, H, "fp8", out_bytes=4, block_size=cache.block_size,
+                              kv_begin=[lo] * B, kv_end=[hi] * B) for lo, hi in bounds)
+    us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
+    res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
+                 "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
+                 "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4),
+                 "launches": S + 1, "note": "8 partition calls + mla_merge_lse"}
+    log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
+    return res
+
+
 def run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
                 stream, result):
     """Causal prefill of the 32K x 12-head workload: parity on sampled tokens, then timing."""
@@ -132,6 +290,8 @@ def main():
     ap.add_argument("--num-splits", type=int, default=0, help="pieces; 0 = automatic plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the other decode / verify configurations")
     ap.add_argument("--no-decode", action="store_true",
                     help="prefill figures only (for profiling the prefill kernel)")
     ap.add_argument("--prefill-steps", type=int, default=5)
@@ -262,13 +422,21 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "decode_kernel<fp8>",
-                     "kernel_us": round(float(kern_ms.mean()) * 1e3, 2)},
+                     "kernel_us": round(float(kern_ms.mean()) * 1e3, 2),
+                     "kernel_us_p10_p50_p90": [round(float(np.percentile(kern_ms, q)) * 1e3, 2)
+                                               for q in (10, 50, 90)]},
     }
 
     # ---------------- prefill (the metric's second half) ----------------
     if not args.no_prefill:
         run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
                     stream, result)
+
+    if not args.no_secondary:
+        result["secondary"] = secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor,
+                                                cache_to_device, check_out, check_lse, dev,
+                                                stream)
+    result["clocks"] = gpu_clocks()
 
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")

@@ -194,9 +194,10 @@ def verify_launcher(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.
                     workspace: Optional[torch.Tensor], num_splits: int = 0,
                     kv_begin: Optional[torch.Tensor] = None,
                     kv_end: Optional[torch.Tensor] = None):
-    """verify's C call with every argument marshalled once: returns a function of no
-    arguments that launches it on the stream current at preparation time.  For loops that
-    launch the same call many times (the tensors must stay alive and keep their storage)."""
+    """verify's C call with every argument marshalled once: returns a function that
+    launches it on torch's current stream of q's device at call time (so the call can be
+    captured into a HIP graph).  For loops that launch the same call many times (the
+    tensors must stay alive and keep their storage)."""
     lib = library()
     if q.dim() != 4 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16 or \
             not q.is_contiguous():
@@ -214,11 +215,11 @@ def verify_launcher(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.
             _ptr(_dev_i32(kv_begin, "kv_begin", dev)), _ptr(_dev_i32(kv_end, "kv_end", dev)),
             B, P, H, int(max_kv_len), float(softmax_scale), _ptr(out), _out_dtype(out.dtype),
             _ptr(lse), int(num_splits), _ptr(workspace),
-            0 if workspace is None else workspace.numel(), _stream(dev))
+            0 if workspace is None else workspace.numel())
     fn = lib.mla_verify
 
     def launch():
-        st = fn(*args)
+        st = fn(*args, _stream(dev))
         if st != 0:
             raise MlaError("mla_verify", st)
     return launch
