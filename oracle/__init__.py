@@ -71,8 +71,29 @@ class OracleLib:
         lib.mla_oracle_merge.argtypes = [P, P, ctypes.c_int, ctypes.c_long, P, P]
         lib.mla_oracle_max_threads.restype = ctypes.c_int
         lib.mla_oracle_max_threads.argtypes = []
+        lib.mla_oracle_fp8_e4m3fn_encode.restype = ctypes.c_uint8
+        lib.mla_oracle_fp8_e4m3fn_encode.argtypes = [ctypes.c_float]
+        lib.mla_oracle_cache_write.restype = ctypes.c_int
+        lib.mla_oracle_cache_write.argtypes = [P, ctypes.c_long, P, P, ctypes.c_int,
+                                               ctypes.c_float, ctypes.c_long]
         self.lib = lib
         self.path = path
+
+    def fp8_e4m3fn_encode(self, y: float) -> int:
+        """E4M3FN code nearest to fp32 y (clamped to +-448, ties to even, NaN -> 0x7F)."""
+        return int(self.lib.mla_oracle_fp8_e4m3fn_encode(ctypes.c_float(y)))
+
+    def cache_write(self, latent_bits: np.ndarray, slot: np.ndarray, kv: np.ndarray,
+                    kv_fp8: bool, kv_scale: float) -> np.ndarray:
+        """Copy of kv [.., 576] (BF16 bits or FP8 codes) with the rows of latent_bits
+        [N, 576] (BF16 bits) written, quantised for FP8, at flat slots `slot` [N]."""
+        lat = _c(latent_bits, np.uint16)
+        sl = _c(slot, np.int32)
+        out = np.ascontiguousarray(kv).copy()
+        num_slots = out.size // 576
+        self.lib.mla_oracle_cache_write(_ptr(lat), lat.shape[0], _ptr(sl), _ptr(out),
+                                         1 if kv_fp8 else 0, float(kv_scale), num_slots)
+        return out
 
     def max_threads(self) -> int:
         return self.lib.mla_oracle_max_threads()
@@ -199,6 +220,14 @@ def decode(*args, **kwargs):
 
 def prefill(*args, **kwargs):
     return get().prefill(*args, **kwargs)
+
+
+def fp8_e4m3fn_encode(y: float) -> int:
+    return get().fp8_e4m3fn_encode(y)
+
+
+def cache_write(*args, **kwargs):
+    return get().cache_write(*args, **kwargs)
 
 
 def merge(*args, **kwargs):

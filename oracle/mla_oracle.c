@@ -288,6 +288,57 @@ int mla_oracle_merge(const double* part_out, const double* part_lse, int S, long
 }
 
 /* Number of OpenMP threads a parallel region would use (0 without OpenMP). */
+/* ---- latent-row cache write: quantise and scatter --------------------------
+ *
+ * New positions' 576-wide latent rows (BF16) go into their cache slots: copied
+ * for a BF16 cache; for an FP8 cache each value x is divided by the per-tensor
+ * scale in fp32 (y = fp32(x / kv_scale), the same real number every reader
+ * multiplies back) and encoded as the E4M3FN code nearest to y after clamping to
+ * the largest finite magnitude 448, ties going to the code with an even
+ * mantissa; a NaN gives code 0x7F.  A row costs 576 FP8 bytes per position (Kimi
+ * K3 engineering report, section "缓存可复用，还要能一致地恢复"); FP8 latent caches
+ * are what the FP8 KV paths store (InferenceX blog on Kimi K2.5, section
+ * "PR #35850 修复了什么"). */
+
+/* Nearest finite E4M3FN code to y, by comparing against every finite code. */
+uint8_t mla_oracle_fp8_e4m3fn_encode(float y) {
+  if (isnan(y)) return 0x7F;
+  const int neg = signbit(y) ? 1 : 0;
+  double a = fabs((double)y);
+  if (a > 448.0) a = 448.0;
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c < 0x7F; ++c) { /* 0x00 .. 0x7E: the non-negative finite codes */
+    const double err = fabs(mla_oracle_fp8_e4m3fn_value((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1) == 1)) {
+      best = c;
+      best_err = err;
+    }
+  }
+  return (uint8_t)(best | (neg << 7));
+}
+
+/* latent [N, 576] BF16 bits; slot [N] (rows with a slot outside [0, num_slots)
+ * are skipped); kv [num_slots, 576] BF16 bits or FP8 codes, updated in place. */
+int mla_oracle_cache_write(const uint16_t* latent, long N, const int32_t* slot, void* kv,
+                           int kv_fp8, float kv_scale, long num_slots) {
+  for (long n = 0; n < N; ++n) {
+    const long s = slot[n];
+    if (s < 0 || s >= num_slots) continue;
+    const uint16_t* x = latent + (size_t)n * ORACLE_DK;
+    if (kv_fp8) {
+      uint8_t* row = (uint8_t*)kv + (size_t)s * ORACLE_DK;
+      for (int d = 0; d < ORACLE_DK; ++d) {
+        const float xf = (float)mla_oracle_bf16_value(x[d]); /* exact */
+        row[d] = mla_oracle_fp8_e4m3fn_encode(xf / kv_scale);
+      }
+    } else {
+      memcpy((uint16_t*)kv + (size_t)s * ORACLE_DK, x, ORACLE_DK * sizeof(uint16_t));
+    }
+  }
+  return 0;
+}
+
 int mla_oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -42,6 +42,14 @@ MUTANTS = [
     ("prefill drops the first key of a sequence", "&v, cu_seqlens[b], g + 1", "&v, cu_seqlens[b] + 1, g + 1"),
     ("sequence index from the wrong stride", "int b = (int)(flat / ((long)H * P));", "int b = (int)(flat % B);"),
     ("BF16 decoded with the wrong shift", "(uint32_t)bits << 16", "(uint32_t)bits << 15"),
+    ("FP8 encoder ties away from zero", "(err == best_err && (c & 1) == 0 && (best & 1) == 1)",
+     "(err == best_err && c > best)"),
+    ("FP8 encoder drops the sign", "return (uint8_t)(best | (neg << 7));", "return (uint8_t)best;"),
+    ("FP8 encoder maps NaN to zero", "if (isnan(y)) return 0x7F;", "if (isnan(y)) return 0x00;"),
+    ("cache write multiplies by the scale", "mla_oracle_fp8_e4m3fn_encode(xf / kv_scale)",
+     "mla_oracle_fp8_e4m3fn_encode(xf * kv_scale)"),
+    ("BF16 cache write to the row index instead of the slot",
+     "memcpy((uint16_t*)kv + (size_t)s * ORACLE_DK", "memcpy((uint16_t*)kv + (size_t)n * ORACLE_DK"),
 ]
 
 
@@ -105,8 +113,38 @@ def pin_zero_query(orc):
         assert lse[b, 0, 0] == math.log(L)
 
 
+def pin_fp8_encoder(orc):
+    finite = [c for c in range(256) if (c & 0x7F) != 0x7F]
+    for c in finite:  # every code round-trips
+        assert orc.fp8_e4m3fn_encode(orc.fp8_e4m3fn_value(c)) == c
+    pos = sorted(c for c in finite if c < 0x80)
+    for a, b in zip(pos[:-1], pos[1:]):  # midpoints tie to the even mantissa
+        mid = (orc.fp8_e4m3fn_value(a) + orc.fp8_e4m3fn_value(b)) / 2
+        assert orc.fp8_e4m3fn_encode(mid) == (a if a % 2 == 0 else b)
+    assert orc.fp8_e4m3fn_encode(math.nan) == 0x7F
+    assert orc.fp8_e4m3fn_encode(-1e9) == 0xFE
+
+
+def pin_cache_write(orc):
+    import torch
+    rng = np.random.default_rng(239)
+    N, num_slots = 24, 64
+    latent = mi.normal_bf16_bits(239, 1, (N, 576))
+    slot = rng.permutation(num_slots)[:N].astype(np.int32)
+    kv8 = np.zeros((num_slots, 576), np.uint8)
+    out8 = orc.cache_write(latent, slot, kv8, True, 0.0123)
+    x = torch.from_numpy(latent.view(np.int16)).view(torch.bfloat16).float()
+    y = torch.clamp(x / torch.tensor(0.0123, dtype=torch.float32), -448, 448)
+    codes = y.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(out8[slot], codes)
+    kv16 = np.zeros((num_slots, 576), np.uint16)
+    out16 = orc.cache_write(latent, slot, kv16, False, 1.0)
+    assert np.array_equal(out16[slot], latent)
+
+
 BATTERY = [pin_decode_bruteforce, pin_decode_fp8_bruteforce, pin_prefill_bruteforce,
-           pin_merge_equals_whole, pin_fp8_codec, pin_zero_query]
+           pin_merge_equals_whole, pin_fp8_codec, pin_zero_query, pin_fp8_encoder,
+           pin_cache_write]
 
 
 def _failures(orc):
