@@ -232,6 +232,35 @@ def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device,
                  "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4),
                  "launches": S + 1, "note": "8 partition calls + mla_merge_lse"}
     log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
+    del kv, part_out, fns
+
+    # cache write: the 32,768 new rows of the prefill workload quantised into a
+    # shuffled FP8 paged cache (64-token blocks)
+    name = "cache_write_t32768_fp8_paged"
+    T = 32768
+    log("generating", name)
+    latent_np = mi.normal_bf16_bits(606, 1, (T, 576))
+    blocks = np.random.default_rng(606).permutation(T // 64 + 8).astype(np.int64)
+    slot_np = (blocks[np.arange(T) // 64] * 64 + np.arange(T) % 64).astype(np.int32)
+    scale = float(np.float32(5.0 / 448.0))
+    latent = bf16_tensor(latent_np, dev).reshape(T, 576)
+    slot_t = torch.from_numpy(slot_np).to(dev)
+    kvc = torch.zeros(((T // 64 + 8) * 64, 576), dtype=torch.uint8, device=dev)
+    mla.cache_write(latent, kvc, slot_t, kv_scale=scale)
+    torch.cuda.synchronize()
+    rows = np.random.default_rng(607).choice(T, 64, replace=False)
+    sub = oracle.cache_write(latent_np[rows], np.arange(64, dtype=np.int32),
+                             np.zeros((64, 576), np.uint8), True, scale)
+    if not np.array_equal(kvc[torch.from_numpy(slot_np[rows]).to(dev)].cpu().numpy(), sub):
+        raise AssertionError(name + ": codes differ from the oracle")
+    ms = event_times(torch, stream, lambda i: mla.cache_write(latent, kvc, slot_t,
+                                                              kv_scale=scale), 50)
+    ab = T * (2 * 576 + 576 + 4)
+    us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
+    res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
+                 "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
+                 "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4)}
+    log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
     return res
 
 

@@ -11,6 +11,7 @@ Entry points (same names as the C-ABI):
   verify(q, kv_cache, block_table, seq_lens, ...)   P query positions, causal among them
   prefill(q, kv, cu_seqlens, ...)                   causal attention of packed sequences
   merge_lse(part_out, part_lse, ...)                merge partials by log-sum-exp
+  cache_write(latent, kv_cache, slot_mapping, ...)  quantise / copy new rows into cache slots
 """
 from __future__ import annotations
 
@@ -60,6 +61,8 @@ def library() -> ctypes.CDLL:
         lib.mla_decode.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, F, P, I, P, I, P, Z, P]
         lib.mla_prefill.restype = I
         lib.mla_prefill.argtypes = [P, P, I, F, P, I, I, I, I, F, P, I, P, P]
+        lib.mla_cache_write.restype = I
+        lib.mla_cache_write.argtypes = [P, ctypes.c_long, P, P, I, F, ctypes.c_long, P]
         lib.mla_merge_lse.restype = I
         lib.mla_merge_lse.argtypes = [P, P, I, I, P, I, P, P]
         lib.mla_decode_workspace_size.restype = Z
@@ -292,6 +295,28 @@ def merge_lse(part_out: torch.Tensor, part_lse: torch.Tensor, *,
                            _stream(dev))
     _check("mla_merge_lse", st)
     return out, lse
+
+
+def cache_write(latent: torch.Tensor, kv_cache: torch.Tensor, slot_mapping: torch.Tensor, *,
+                kv_scale: float = 1.0) -> torch.Tensor:
+    """Write latent [N, 576] bf16 rows into kv_cache [num_blocks, block_size, 576] at flat
+    slots slot_mapping [N] int32 (negative or out-of-range slots are skipped); FP8 caches
+    (uint8 / float8_e4m3fn) receive E4M3FN codes of x / kv_scale.  Returns kv_cache."""
+    lib = library()
+    if latent.dim() != 2 or latent.shape[1] != HEAD_DIM_K or latent.dtype != torch.bfloat16:
+        raise TypeError("latent must be [N, 576] bfloat16")
+    dev = latent.device
+    if kv_cache.shape[-1] != HEAD_DIM_K or kv_cache.device != dev or not kv_cache.is_contiguous():
+        raise TypeError("kv_cache must be a contiguous [..., 576] tensor on the latent's device")
+    latent = latent.contiguous()
+    sm = _dev_i32(slot_mapping, "slot_mapping", dev)
+    if sm.numel() != latent.shape[0]:
+        raise TypeError("slot_mapping must have one entry per latent row")
+    st = lib.mla_cache_write(_ptr(latent), latent.shape[0], _ptr(sm), _ptr(kv_cache),
+                             _kv_dtype(kv_cache), float(kv_scale),
+                             kv_cache.numel() // HEAD_DIM_K, _stream(dev))
+    _check("mla_cache_write", st)
+    return kv_cache
 
 
 def default_softmax_scale(qk_dim: int = 192) -> float:

@@ -218,6 +218,22 @@ mla_status mla_merge_lse(const float* part_out, const float* part_lse, int S, in
   return MLA_OK;
 }
 
+mla_status mla_cache_write(const void* latent, long N, const int32_t* slot_mapping,
+                           void* kv_cache, int kv_dtype, float kv_scale, long num_slots,
+                           void* stream) {
+  if (N < 0 || num_slots < 0) return MLA_E_INVAL;
+  if (kv_dtype != MLA_DTYPE_BF16 && kv_dtype != MLA_DTYPE_FP8_E4M3) return MLA_E_UNSUPPORTED;
+  if (kv_dtype == MLA_DTYPE_FP8_E4M3 && !finite_positive(kv_scale)) return MLA_E_INVAL;
+  if (N == 0) return MLA_OK;
+  if (!latent || !slot_mapping || !kv_cache) return MLA_E_INVAL;
+  if (N > 0x7fffffffL / 36) return MLA_E_UNSUPPORTED;
+  const hipError_t e =
+      mla_impl::launch_cache_write(static_cast<const uint16_t*>(latent), N, slot_mapping,
+                                   kv_cache, kv_dtype == MLA_DTYPE_FP8_E4M3, kv_scale, num_slots,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_E_LAUNCH;
+}
+
 mla_status mla_prefill(const void* q, const void* kv, int kv_dtype, float kv_scale,
                        const int32_t* cu_seqlens, int B, int T, int max_seqlen, int H,
                        float softmax_scale, void* out, int out_dtype, float* lse, void* stream) {

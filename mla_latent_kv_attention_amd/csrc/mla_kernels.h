@@ -42,6 +42,11 @@ hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream)
 hipError_t launch_merge(const float* part_out, const float* part_lse, int S, int N, void* out,
                         int out_bf16, float* lse, hipStream_t stream);
 
+// Quantise (FP8) or copy (BF16) N latent rows into cache slots slot[n] of a cache
+// with num_slots rows; slots outside [0, num_slots) are skipped.
+hipError_t launch_cache_write(const uint16_t* latent, long N, const int32_t* slot, void* kv,
+                              bool kv_fp8, float kv_scale, long num_slots, hipStream_t stream);
+
 struct PrefillParams {
   const uint16_t* q;           // [T, H, 576]
   const uint8_t* kv;           // [T, 576] bf16 or fp8 codes

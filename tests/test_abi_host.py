@@ -30,7 +30,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ["mla_decode", "mla_verify", "mla_prefill", "mla_merge_lse",
+    for n in ["mla_decode", "mla_verify", "mla_prefill", "mla_merge_lse", "mla_cache_write",
               "mla_decode_workspace_size", "mla_decode_num_splits", "mla_status_string",
               "mla_version"]:
         assert n in names
@@ -99,6 +99,19 @@ def test_merge_rejects_bad_arguments(lib):
     assert lib.mla_merge_lse(P, P, 2, 4, P, 1, None, None) == -2
     assert lib.mla_merge_lse(None, P, 2, 4, P, 2, None, None) == -1
     assert lib.mla_merge_lse(None, None, 2, 0, None, 2, None, None) == 0
+
+
+def test_cache_write_rejects_bad_arguments(lib):
+    P = ctypes.c_void_p(0x1000)
+    lib.mla_cache_write.argtypes = [ctypes.c_void_p, ctypes.c_long, ctypes.c_void_p,
+                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_long,
+                                    ctypes.c_void_p]
+    assert lib.mla_cache_write(P, -1, P, P, 1, 0.01, 64, None) == -1
+    assert lib.mla_cache_write(P, 4, P, P, 2, 0.01, 64, None) == -2   # FP32 is no cache dtype
+    assert lib.mla_cache_write(P, 4, P, P, 1, 0.0, 64, None) == -1    # FP8 needs a scale > 0
+    assert lib.mla_cache_write(None, 4, P, P, 1, 0.01, 64, None) == -1
+    assert lib.mla_cache_write(P, 4, None, P, 0, 1.0, 64, None) == -1
+    assert lib.mla_cache_write(None, 0, None, None, 0, 1.0, 0, None) == 0
 
 
 def test_prefill_rejects_bad_arguments(lib):
