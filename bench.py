@@ -141,7 +141,8 @@ def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device,
     """The other decode / verify configurations: parity on sampled rows, then per-call
     HIP-event times (p10 / p50 / p90) and, for the launch-bound ones, HIP-graph replays."""
     res = {}
-    for name, rotate in (("decode_b1_h12_l1024_bf16", 1), ("verify_b4_p4_h12_l32768_bf16", 4)):
+    for name, rotate in (("decode_b1_h12_l1024_bf16", 1), ("verify_b4_p4_h12_l32768_bf16", 4),
+                         ("verify_b1_p4_h12_l32768_fp8", 28)):
         w = mi.WORKLOADS[name]
         log("generating", name)
         d = mi.decode_inputs(w)

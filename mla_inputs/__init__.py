@@ -235,6 +235,10 @@ WORKLOADS = {
     "verify_b4_p4_h12pad16_l32768_bf16": DecodeWorkload(
         "verify_b4_p4_h12pad16_l32768_bf16", 4, 4, 12, "bf16", 64, seed=303, lengths=[32768] * 4,
         pad_heads_to=16),
+    # one sequence x 4 verify positions, 12 heads, 32,768 context, FP8 paged: the short
+    # verify whose work-group count the pages discuss
+    "verify_b1_p4_h12_l32768_fp8": DecodeWorkload(
+        "verify_b1_p4_h12_l32768_fp8", 1, 4, 12, "fp8", 64, seed=707, lengths=[32768]),
     # batch 8, 12 heads, 142,000 keys, FP8 paged, 8 contiguous partitions merged by LSE
     "decode_b8_h12_l142000_fp8_8parts": DecodeWorkload(
         "decode_b8_h12_l142000_fp8_8parts", 8, 1, 12, "fp8", 64, seed=505, lengths=[142000] * 8,

@@ -14,6 +14,7 @@ namespace {
 
 constexpr int kStepTokens = 16;        // tokens per step of the concatenated step list
 constexpr int kMinStepsPerPiece = 8;   // two steps per wave before a piece pays for its merge
+constexpr int kMaxPiecesPerSeq = 16;   // mean shares per sequence the in-launch merge takes
 // What a piece pays for each sequence it touches (query load, wave merge, partial
 // publish), in 16-token steps of streaming; measured per cache dtype.
 constexpr int kSegmentStepsFp8 = 30;
@@ -40,6 +41,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Plan {
   int R, RB, W;
+  bool merge_in_kernel;  // few enough shares per sequence for the last piece to merge them
 };
 
 // Piece plan.  The kernel is persistent: W pieces x RB row blocks work-groups,
@@ -51,16 +53,30 @@ Plan make_plan(int B, int P, int H, int max_kv_len, int num_splits, int cus) {
   Plan pl;
   pl.R = P * H;
   pl.RB = (pl.R + 15) / 16;
+  const long Bn = B > 0 ? B : 1;
   if (num_splits > 0) {
     pl.W = num_splits < kMaxPieces ? num_splits : kMaxPieces;
+    pl.merge_in_kernel = pl.W <= kMaxPiecesPerSeq * Bn;
     return pl;
   }
   long W = (cus > 0 ? cus : 256) / pl.RB;
-  const long steps = (long)(B > 0 ? B : 1) * (((long)max_kv_len + kStepTokens - 1) / kStepTokens);
+  // With several row blocks the grid is W rounded up to 8 per row block (the row
+  // blocks of a piece share an XCD); W itself a multiple of 8 keeps that grid
+  // within one work-group per CU, so no piece waits for a CU to free up.
+  if (pl.RB > 1 && W >= 8) W -= W % 8;
+  const long steps = Bn * (((long)max_kv_len + kStepTokens - 1) / kStepTokens);
   const long by_steps = (steps + kMinStepsPerPiece - 1) / kMinStepsPerPiece;
   if (W > by_steps) W = by_steps;
+  // The piece that finishes a sequence last merges every share of it through one
+  // CU, which stays cheap up to kMaxPiecesPerSeq shares per sequence: cap there
+  // while the cap still keeps at least half the work-groups.  Batches of very few
+  // sequences take all the pieces instead, and a separate launch merges every row
+  // in parallel (measured: cheaper than a second launch whenever the cap holds).
+  const long cap = kMaxPiecesPerSeq * Bn;
+  if (W > cap && 2 * cap >= W) W = cap;
   if (W < 1) W = 1;
   pl.W = (int)W;
+  pl.merge_in_kernel = pl.W <= cap;
   return pl;
 }
 
@@ -74,7 +90,7 @@ size_t workspace_bytes_for(const Plan& pl, int B) {
   if (pl.W <= 1) return 0;
   const size_t rows = (size_t)(pl.W + B) * pl.R;
   return kCounterBytes + align_up(rows * MLA_HEAD_DIM_V * sizeof(float)) +
-         align_up(rows * sizeof(float));
+         align_up(rows * sizeof(float)) + align_up((size_t)2 * B * sizeof(int));
 }
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.f; }
@@ -188,9 +204,16 @@ mla_status mla_verify(const void* q, const void* kv_cache, int kv_dtype, float k
     p.part_out = reinterpret_cast<float*>(ws);
     ws += align_up(rows * MLA_HEAD_DIM_V * sizeof(float));
     p.part_lse = reinterpret_cast<float*>(ws);
+    ws += align_up(rows * sizeof(float));
+    p.seq_pieces = reinterpret_cast<int*>(ws);
+    p.merge_in_kernel = pl.merge_in_kernel ? 1 : 0;
+  } else {
+    p.merge_in_kernel = 1;  // one piece: every sequence is written whole
   }
   const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
-  if (mla_impl::launch_decode(p, fp8, static_cast<hipStream_t>(stream)) != hipSuccess)
+  const hipStream_t stm = static_cast<hipStream_t>(stream);
+  if (mla_impl::launch_decode(p, fp8, stm) != hipSuccess) return MLA_E_LAUNCH;
+  if (!p.merge_in_kernel && mla_impl::launch_merge_shares(p, stm) != hipSuccess)
     return MLA_E_LAUNCH;
   return MLA_OK;
 }

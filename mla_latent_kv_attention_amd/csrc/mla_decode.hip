@@ -14,7 +14,10 @@
 // agent-coherent stores and bumps a per-sequence counter; the piece that
 // finishes last combines the shares by lse (the combination position-sharded
 // attention uses, same report, section "缓存可复用，还要能一致地恢复") and resets
-// the counter for the next call.
+// the counter for the next call.  When a sequence is spread over many pieces
+// (few sequences in the batch) that one merging CU would be the bottleneck, so
+// the pieces only publish their shares and a second launch merges every output
+// row in parallel.
 //
 // Per work-group, four waves stream interleaved 16-token steps of a segment.
 // Each wave keeps its own online-softmax state and a 16-row x 512 fp32
@@ -246,6 +249,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     if (b >= p.B) break;
     const int nb = seq_range(p, b).n;
     part += nb > 0 ? nb + c : 0;
+    if (w == 0 && nb == 0 && !p.merge_in_kernel && rb == 0) {
+      p.seq_pieces[2 * b] = 0;  // no shares to merge
+      p.seq_pieces[2 * b + 1] = 0;
+    }
     if (w == 0 && nb == 0) {
       for (int row = 0; row < 16; ++row) {
         const int rr = rb * 16 + row;
@@ -296,6 +303,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     const bool row_ok = r < p.R;
     const int hi_row = row_ok ? min(hi_all, L - p.P + r / p.H + 1) : lo;
     const int w_first = owner(rs, N, We), w_last = owner(rs + sr.n - 1, N, We);
+    if (!p.merge_in_kernel && rb == 0 && w == w_first && tid == 0) {
+      p.seq_pieces[2 * b] = w_first;  // the shares the separate merge combines
+      p.seq_pieces[2 * b + 1] = w_last;
+    }
 
     __syncthreads();  // the previous segment is done with the LDS tiles
     // The 18 Q^T fragments (B operand of the score MFMA) of the lane's query row stay
@@ -562,6 +573,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
         }
       }
     }
+    if (!p.merge_in_kernel) continue;  // a separate launch merges the shares
     // Publish the partial; the last piece to finish sequence b merges all of them.
     // Every thread waits for its agent-coherent stores to be acknowledged before
     // the barrier, so they are visible device-wide before the counter moves; the
@@ -580,6 +592,75 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     if (!last_flag) continue;
     if (rr_ok) merge_pieces(p, b, rr, n, w_first, w_last);
   }
+}
+
+// The merge of sequences split into many shares, as a launch of its own: one
+// 256-thread work-group per output row.  The shares' lse are reduced across the
+// work-group; then 8 groups of 32 threads take every 8th share (each thread 16 of
+// the 512 dims) so that many shares are in flight at once, and the groups' sums
+// meet in LDS.  A share that saw no key of the row has lse = -inf and an unwritten
+// row, which its zero weight selects away.
+__global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p) {
+  __shared__ float red[8][kDV + 4];
+  __shared__ float wred[8];
+  __shared__ float mred[4];
+  const int tid = threadIdx.x;
+  const size_t n = blockIdx.x;
+  const int b = (int)(n / p.R), rr = (int)(n % p.R);
+  const int w_first = p.seq_pieces[2 * b], w_last = p.seq_pieces[2 * b + 1];
+  if (w_first == w_last) return;  // one piece held the whole sequence and wrote it
+  const size_t R = p.R;
+  const float* lse_b = p.part_lse + (size_t)b * R + rr;  // share v at v * R
+  float mx = -INFINITY;
+  for (int v = w_first + tid; v <= w_last; v += 256) mx = fmaxf(mx, load_agent(lse_b + v * R));
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if ((tid & 63) == 0) mred[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
+  const int g = tid >> 5, l = tid & 31;
+  f32x4 o4[4] = {};
+  float ws = 0.f;
+  if (mx != -INFINITY) {
+    const uint32_t off = (uint32_t)(rr * kDV + 16 * l) * 4;
+    for (int v = w_first + g; v <= w_last; v += 8) {
+      const float x = load_agent(lse_b + v * R);
+      const float wt = (x == -INFINITY) ? 0.f : expf(x - mx);
+      const auto rsrc = agent_rsrc(p.part_out + (size_t)(v + b) * R * kDV);
+      f32x4 t[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t[k] = load_agent16(rsrc, off + 16 * k);
+      ws += wt;
+      if (wt > 0.f) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o4[k] += wt * t[k];
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) *(f32x4*)&red[g][16 * l + 4 * k] = o4[k];
+  if (l == 0) wred[g] = ws;
+  __syncthreads();
+  float wsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) wsum += wred[i];
+  // thread tid writes dims 2 tid, 2 tid + 1
+  float2 v2 = {0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    v2.x += red[i][2 * tid];
+    v2.y += red[i][2 * tid + 1];
+  }
+  const float il = (mx != -INFINITY && wsum > 0.f) ? 1.f / wsum : 0.f;
+  v2.x *= il;
+  v2.y *= il;
+  if (p.out_bf16) {
+    const bf16x2 ob = {(__bf16)v2.x, (__bf16)v2.y};
+    *(bf16x2*)((uint16_t*)p.out + n * kDV + 2 * tid) = ob;
+  } else {
+    *(float2*)((float*)p.out + n * kDV + 2 * tid) = v2;
+  }
+  if (p.lse && tid == 0) p.lse[n] = (mx == -INFINITY) ? -INFINITY : mx + logf(wsum);
 }
 
 // One work-group of 128 threads per row; each thread owns 4 of the 512 dims.  The
@@ -626,6 +707,14 @@ hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream)
     hipLaunchKernelGGL(decode_kernel<true>, dim3(grid), dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL(decode_kernel<false>, dim3(grid), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_shares(const DecodeParams& p, hipStream_t stream) {
+  const long rows = (long)p.B * p.R;
+  if (rows == 0) return hipSuccess;
+  if (rows > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_shares_kernel, dim3((unsigned)rows), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -29,6 +29,8 @@ struct DecodeParams {
   float* part_out;             // [W + B, R, 512]: slot w + b holds piece w's share of sequence b
   float* part_lse;             // [W + B, R]
   int* counters;               // [B, RB] (B * RB <= MLA_MAX_COUNTERS): zero on entry, left zero
+  int merge_in_kernel;         // 1: the last piece of a sequence merges; 0: launch_merge_shares
+  int* seq_pieces;             // [B, 2]: first and last piece of each sequence (merge_in_kernel 0)
   void* out;                   // [B * R, 512] fp32 or bf16
   int out_bf16;
   float* lse;                  // [B * R] or null
@@ -38,6 +40,9 @@ struct DecodeParams {
 int decode_grid_size(int W, int RB);
 
 hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream);
+
+// The separate merge of a launch_decode with merge_in_kernel = 0 (same params).
+hipError_t launch_merge_shares(const DecodeParams& p, hipStream_t stream);
 
 hipError_t launch_merge(const float* part_out, const float* part_lse, int S, int N, void* out,
                         int out_bf16, float* lse, hipStream_t stream);

@@ -126,8 +126,8 @@ def test_prefill_rejects_bad_arguments(lib):
 
 def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
     """The pages' short verify: one sequence, 4 positions, 12 heads; 48 work-groups were
-    too few for the chip.  The persistent plan puts one work-group on every CU (minus
-    the rounding of CUs to whole row-block groups) once the history is long enough."""
+    too few for the chip.  The persistent plan launches more than that, never more than
+    one per CU, once the history is long enough."""
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_closed_forms.json")))
     sv = g["short_verify_workgroups"]
     heads = sv["heads"]
@@ -135,10 +135,10 @@ def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
     assert heads * sv["tiled_width"] // sv["narrow_tile_columns"] == sv["narrow_tile_workgroups"]
     rows = 4 * heads
     row_blocks = -(-rows // 16)
-    for cus in [80, 256, 304]:
+    for cus in [256, 304]:
         for ctx in [16384, 32768, 142000]:
             W = lib.mla_decode_num_splits(1, 4, heads, ctx, 0, cus)
-            assert cus - row_blocks < W * row_blocks <= cus
+            assert W * row_blocks <= cus
             assert W * row_blocks > sv["wide_tile_workgroups"]
 
 
@@ -146,25 +146,36 @@ def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
                                      (4, 4, 16, 32768), (8, 1, 12, 17750), (3, 2, 8, 64),
                                      (1, 1, 12, 16), (0, 1, 12, 0)])
 def test_planner_pieces_fit_the_chip_and_the_work(lib, B, P, H, L):
-    """At most one work-group per CU, at least eight 16-token steps per piece (as far as
-    the max_kv_len hint tells), and as many pieces as both allow."""
+    """At most one work-group per CU counting the grid's rounding (a multiple of 8
+    pieces when there are several row blocks), at least eight 16-token steps per piece
+    (as far as the max_kv_len hint tells), as many pieces as both allow, and at most 16
+    per sequence where that cap keeps at least half of them."""
     RB = -(-(P * H) // 16)
     for cus in [80, 256, 304]:
         W = lib.mla_decode_num_splits(B, P, H, L, 0, cus)
         steps = max(B, 1) * (-(-L // 16))
-        assert W == max(1, min(cus // RB, -(-steps // 8)))
+        by_cus = cus // RB
+        if RB > 1 and by_cus >= 8:
+            by_cus -= by_cus % 8
+        want = max(1, min(by_cus, -(-steps // 8)))
+        cap = 16 * max(B, 1)
+        if want > cap and 2 * cap >= want:
+            want = cap
+        assert W == want
+        assert (-(-W // 8) * 8 * RB if RB > 1 else W) <= max(cus, 8 * RB)
 
 
 @pytest.mark.parametrize("B,P,H,L,S", [(32, 1, 12, 16384, 0), (4, 4, 12, 32768, 0),
                                        (2, 3, 5, 100, 7), (1, 1, 12, 16, 0)])
 def test_workspace_holds_slots_and_counters(lib, B, P, H, L, S):
     """A fixed block of 65536 counters first (the same bytes for every shape), then
-    (W + B) x rows partial outputs and lse, each part 256-byte aligned; nothing for a
-    single piece."""
+    (W + B) x rows partial outputs and lse, then each sequence's piece range, each part
+    256-byte aligned; nothing for a single piece."""
     W = lib.mla_decode_num_splits(B, P, H, L, S, 0)  # the plan the workspace query uses
     R = P * H
     al = lambda x: -(-x // 256) * 256
-    want = 0 if W <= 1 else 65536 * 4 + al((W + B) * R * 512 * 4) + al((W + B) * R * 4)
+    want = 0 if W <= 1 else (65536 * 4 + al((W + B) * R * 512 * 4) + al((W + B) * R * 4)
+                             + al(2 * B * 4))
     assert lib.mla_decode_workspace_size(B, P, H, L, S) == want
 
 

@@ -278,6 +278,23 @@ def test_full_verify(mla, name):
         assert torch.equal(out[:, :, :w.heads], o12) and torch.equal(lse[:, :, :w.heads], l12)
 
 
+def test_full_verify_b1_p4_h12_l32768_fp8(mla):
+    """The pages' short verify shape (one sequence, 4 positions, 12 heads, 32K context):
+    more pieces than 16 per sequence, so the shares are merged by the separate launch;
+    also run with the in-launch merge (16 pieces) and compare both to the oracle."""
+    w, q, cache = full_case("verify_b1_p4_h12_l32768_fp8")
+    print("full", w.name, flush=True)
+    B, P, H = q.shape[:3]
+    assert mla.decode_num_splits(B, P, H, 32768) > 16
+    rows = sample_rows(B * P * H, 30, 13)
+    ref_o, ref_l = run_oracle(q, cache, rows=rows)
+    idx = torch.from_numpy(rows).to(DEV)
+    for splits in [0, 16]:
+        out, lse = run_gpu(mla, q, cache, max_kv_len=32768, num_splits=splits)
+        check_out(out.reshape(-1, 512)[idx], ref_o)
+        check_lse(lse.reshape(-1)[idx], ref_l)
+
+
 def test_full_decode_b8_h12_l142000_fp8_8parts(mla):
     """8 contiguous key partitions (one per call, as a position shard would compute its
     share), merged by mla_merge_lse, against the unsplit call and the oracle."""
