@@ -623,17 +623,26 @@ __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p)
   float ws = 0.f;
   if (mx != -INFINITY) {
     const uint32_t off = (uint32_t)(rr * kDV + 16 * l) * 4;
-    for (int v = w_first + g; v <= w_last; v += 8) {
-      const float x = load_agent(lse_b + v * R);
-      const float wt = (x == -INFINITY) ? 0.f : expf(x - mx);
-      const auto rsrc = agent_rsrc(p.part_out + (size_t)(v + b) * R * kDV);
-      f32x4 t[4];
+    // four of the group's shares per iteration, all their loads in flight together
+    for (int v0 = w_first + g; v0 <= w_last; v0 += 32) {
+      float wt[4];
+      f32x4 t[4][4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) t[k] = load_agent16(rsrc, off + 16 * k);
-      ws += wt;
-      if (wt > 0.f) {
+      for (int u = 0; u < 4; ++u) {
+        const int v = min(v0 + 8 * u, w_last);  // past the end: re-read, weight 0
+        const float x = load_agent(lse_b + v * R);
+        wt[u] = (v0 + 8 * u <= w_last && x != -INFINITY) ? expf(x - mx) : 0.f;
+        const auto rsrc = agent_rsrc(p.part_out + (size_t)(v + b) * R * kDV);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o4[k] += wt * t[k];
+        for (int k = 0; k < 4; ++k) t[u][k] = load_agent16(rsrc, off + 16 * k);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        ws += wt[u];
+        if (wt[u] > 0.f) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) o4[k] += wt[u] * t[u][k];
+        }
       }
     }
   }
