@@ -15,7 +15,11 @@ datasets and weights are not used):
     (sequence, logical block) is drawn from a seeded permutation of the pool;
     table entries past a sequence's last block point at a NaN-filled spare
     block; slots past a sequence's length and all spare blocks hold NaN;
-  * per-sequence lengths: seeded uniform integers in the stated inclusive range.
+  * per-sequence lengths: seeded uniform integers in the stated inclusive range;
+  * probability rows (input of the top-k renormalisation): logits iid
+    N(0, sigma^2) in float64 (sigma = 3 gives a peaked, long-tailed row), turned
+    into probabilities by exp(logit - max) / sum in float64 and rounded to
+    float32; per-row k: seeded uniform integers in the stated inclusive range.
 """
 from __future__ import annotations
 
@@ -215,6 +219,43 @@ def prefill_inputs(w: PrefillWorkload) -> Dict[str, object]:
     cu = np.zeros(len(w.seq_lens) + 1, np.int32)
     cu[1:] = np.cumsum(w.seq_lens)
     return {"q": q, "kv": kv, "kv_scale": scale, "cu_seqlens": cu}
+
+
+def probability_rows(seed: int, rows: int, vocab: int, sigma: float = 3.0,
+                     stream: int = 11) -> np.ndarray:
+    """[rows, vocab] float32 rows of a softmax over N(0, sigma^2) logits."""
+    out = np.empty((rows, vocab), np.float32)
+    rng = rng_for(seed, stream)
+    for r in range(rows):
+        z = rng.standard_normal(vocab) * sigma
+        e = np.exp(z - z.max())
+        out[r] = (e / e.sum()).astype(np.float32)
+    return out
+
+
+@dataclasses.dataclass
+class TopKWorkload:
+    name: str
+    rows: int
+    vocab: int
+    k_range: tuple  # inclusive
+    seed: int
+
+    def top_k(self) -> np.ndarray:
+        lo, hi = self.k_range
+        return rng_for(self.seed, 12).integers(lo, hi + 1, size=self.rows).astype(np.int32)
+
+    def probs(self) -> np.ndarray:
+        return probability_rows(self.seed, self.rows, self.vocab)
+
+
+# Top-k renormalisation of the target probabilities after a verify step: 32 sequences x
+# 4 verify positions = 128 rows over a 163,840-entry vocabulary (the published Kimi K2
+# tokenizer size; the pages give none), k drawn per row in [1, 100].
+TOP_K_WORKLOADS = {
+    "top_k_renorm_r128_v163840": TopKWorkload("top_k_renorm_r128_v163840", 128, 163840,
+                                              (1, 100), seed=808),
+}
 
 
 # The five workloads the measurements are quoted on.

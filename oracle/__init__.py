@@ -7,8 +7,9 @@ this module only builds it with gcc and marshals numpy arrays.
 
 Functions follow the plain definitions stated in ``mla_oracle.c``: softmax
 attention of each query row over its visible latent rows (key = the whole
-576-wide row, value = its first 512 entries), and the merge of partial results
-by their log-sum-exp normalisers.
+576-wide row, value = its first 512 entries), the merge of partial results
+by their log-sum-exp normalisers, the latent-row cache write (FP8 E4M3FN
+quantisation and scatter) and the top-k renormalisation of probability rows.
 """
 from __future__ import annotations
 
@@ -76,6 +77,8 @@ class OracleLib:
         lib.mla_oracle_cache_write.restype = ctypes.c_int
         lib.mla_oracle_cache_write.argtypes = [P, ctypes.c_long, P, P, ctypes.c_int,
                                                ctypes.c_float, ctypes.c_long]
+        lib.mla_oracle_top_k_renorm.restype = ctypes.c_int
+        lib.mla_oracle_top_k_renorm.argtypes = [P, P, ctypes.c_long, ctypes.c_long, P]
         self.lib = lib
         self.path = path
 
@@ -93,6 +96,21 @@ class OracleLib:
         num_slots = out.size // 576
         self.lib.mla_oracle_cache_write(_ptr(lat), lat.shape[0], _ptr(sl), _ptr(out),
                                          1 if kv_fp8 else 0, float(kv_scale), num_slots)
+        return out
+
+    def top_k_renorm_prob(self, probs: np.ndarray, top_k) -> np.ndarray:
+        """Rows of fp32 probabilities -> float64 rows: the k largest entries of each row
+        divided by their sum, every other entry zero (k per row; k <= 0 or k >= vocab
+        keeps the whole row; ties rank the lower index first)."""
+        p = _c(probs, np.float32)
+        if p.ndim != 2:
+            raise ValueError("probs must be [rows, vocab]")
+        rows, vocab = p.shape
+        k = np.ascontiguousarray(np.broadcast_to(np.asarray(top_k, np.int32), (rows,)))
+        out = np.empty((rows, vocab), np.float64)
+        st = self.lib.mla_oracle_top_k_renorm(_ptr(p), _ptr(k), rows, vocab, _ptr(out))
+        if st != 0:
+            raise ValueError("oracle top_k_renorm failed (%d): NaN entry or no memory" % st)
         return out
 
     def max_threads(self) -> int:
@@ -232,3 +250,7 @@ def cache_write(*args, **kwargs):
 
 def merge(*args, **kwargs):
     return get().merge(*args, **kwargs)
+
+
+def top_k_renorm_prob(*args, **kwargs):
+    return get().top_k_renorm_prob(*args, **kwargs)

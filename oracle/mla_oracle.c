@@ -32,6 +32,9 @@
  *        M = max_p lse_p,  lse = M + ln sum_p exp(lse_p - M),
  *        out = sum_p exp(lse_p - lse) out_p;  all lse_p = -inf gives 0 / -inf.
  *
+ *  - Latent-row cache write and top-k renormalisation of probability rows: see
+ *    the comments above mla_oracle_cache_write and mla_oracle_top_k_renorm.
+ *
  * Inputs are the raw bytes both paths consume: BF16 bit patterns for queries
  * and BF16 caches, OCP FP8 E4M3FN codes plus one fp32 per-tensor scale for FP8
  * caches.  Every input value is decoded exactly into a double; the product of
@@ -345,4 +348,66 @@ int mla_oracle_max_threads(void) {
 #else
   return 0;
 #endif
+}
+
+/*
+ * Top-k renormalisation of probability rows, the acceptance-sampling step that
+ * follows speculative verify (tahou.com article, section "ROCm适配迎来突破，软件
+ * 壁垒不再高不可攀"; 66bd.net article, section "我们是如何做到的"): of each row,
+ * keep the k largest entries, set every other entry to zero and divide the kept
+ * ones by their sum, so the row sums to one again.
+ *
+ * Readings where the pages say no more:
+ *  - exactly k entries are kept; entries rank by value, a -0 below a +0, and
+ *    among equal values the lower index ranks first;
+ *  - k <= 0 or k >= vocab keeps the whole row (renormalisation only);
+ *  - a kept sum of zero gives a row of zeros;
+ *  - NaN entries have no rank: the call returns -1.
+ * The ranking is a plain sort with that order; the sum is taken in double.
+ */
+typedef struct {
+  float v;
+  long i;
+} oracle_entry;
+
+/* -1 when a ranks before b (a is "larger" in the order above). */
+static int oracle_rank_cmp(const void* pa, const void* pb) {
+  const oracle_entry* a = (const oracle_entry*)pa;
+  const oracle_entry* b = (const oracle_entry*)pb;
+  if (a->v > b->v) return -1;
+  if (a->v < b->v) return 1;
+  const int sa = signbit(a->v) ? 1 : 0, sb = signbit(b->v) ? 1 : 0;
+  if (sa != sb) return sa ? 1 : -1; /* equal values differing in sign: both zero */
+  return (a->i < b->i) ? -1 : (a->i > b->i);
+}
+
+int mla_oracle_top_k_renorm(const float* probs, const int32_t* top_k, long rows, long vocab,
+                            double* out) {
+  for (long n = 0; n < rows * vocab; ++n)
+    if (isnan(probs[n])) return -1;
+  int status = 0;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (long r = 0; r < rows; ++r) {
+    const float* p = probs + r * vocab;
+    double* o = out + r * vocab;
+    oracle_entry* e = (oracle_entry*)malloc((size_t)(vocab > 0 ? vocab : 1) * sizeof(oracle_entry));
+    if (!e) {
+#pragma omp atomic write
+      status = -2;
+      continue;
+    }
+    for (long i = 0; i < vocab; ++i) {
+      e[i].v = p[i];
+      e[i].i = i;
+    }
+    qsort(e, (size_t)vocab, sizeof(oracle_entry), oracle_rank_cmp);
+    const long k = (top_k[r] <= 0 || top_k[r] >= vocab) ? vocab : top_k[r];
+    double sum = 0.0;
+    for (long j = 0; j < k; ++j) sum += (double)e[j].v;
+    for (long i = 0; i < vocab; ++i) o[i] = 0.0;
+    if (sum != 0.0)
+      for (long j = 0; j < k; ++j) o[e[j].i] = (double)e[j].v / sum;
+    free(e);
+  }
+  return status;
 }

@@ -48,6 +48,15 @@ MUTANTS = [
     ("FP8 encoder maps NaN to zero", "if (isnan(y)) return 0x7F;", "if (isnan(y)) return 0x00;"),
     ("cache write multiplies by the scale", "mla_oracle_fp8_e4m3fn_encode(xf / kv_scale)",
      "mla_oracle_fp8_e4m3fn_encode(xf * kv_scale)"),
+    ("top-k ties ranked toward the higher index", "return (a->i < b->i) ? -1 : (a->i > b->i);",
+     "return (a->i > b->i) ? -1 : (a->i < b->i);"),
+    ("top-k keeps the smallest entries", "if (a->v > b->v) return -1;", "if (a->v < b->v) return -1;"),
+    ("top-k keeps one entry too many", "for (long j = 0; j < k; ++j) o[e[j].i]",
+     "for (long j = 0; j <= k && j < vocab; ++j) o[e[j].i]"),
+    ("top-k normalises by the whole row", "for (long j = 0; j < k; ++j) sum +=",
+     "for (long j = 0; j < vocab; ++j) sum +="),
+    ("top-k treats k = 0 as keep none", "(top_k[r] <= 0 || top_k[r] >= vocab)",
+     "(top_k[r] < 0 || top_k[r] >= vocab)"),
     ("BF16 cache write to the row index instead of the slot",
      "memcpy((uint16_t*)kv + (size_t)s * ORACLE_DK", "memcpy((uint16_t*)kv + (size_t)n * ORACLE_DK"),
 ]
@@ -142,9 +151,20 @@ def pin_cache_write(orc):
     assert np.array_equal(out16[slot], latent)
 
 
+def pin_top_k(orc):
+    from test_oracle_top_k import torch_reference, tied_rows
+    p = np.concatenate([mi.probability_rows(241, 4, 500), tied_rows(243, 4, 500, 5)])
+    ks = np.array([1, 7, 0, 250, 3, 60, 499, 500], np.int32)
+    out = orc.top_k_renorm_prob(p, ks)
+    for r, k in enumerate(ks):
+        kept, ref = torch_reference(p[r], k)
+        assert np.array_equal(out[r] != 0, kept)
+        assert np.max(np.abs(out[r] - ref)) < 1e-12
+
+
 BATTERY = [pin_decode_bruteforce, pin_decode_fp8_bruteforce, pin_prefill_bruteforce,
            pin_merge_equals_whole, pin_fp8_codec, pin_zero_query, pin_fp8_encoder,
-           pin_cache_write]
+           pin_cache_write, pin_top_k]
 
 
 def _failures(orc):
