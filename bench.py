@@ -262,6 +262,52 @@ def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device,
                  "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
                  "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4)}
     log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
+    del latent, kvc
+
+    # top-k renormalisation of the target probabilities after a verify step: 128 rows
+    # (32 sequences x 4 positions) over a 163,840-entry vocabulary, k per row in [1, 100];
+    # 7 rotating copies of the 84 MB input so every call reads HBM
+    name = "top_k_renorm_r128_v163840"
+    w = mi.TOP_K_WORKLOADS[name]
+    log("generating", name)
+    p_np, k_np = w.probs(), w.top_k()
+    copies = 7
+    pin = [torch.from_numpy(p_np).to(dev) for _ in range(copies)]
+    pout = [torch.empty_like(pin[0]) for _ in range(copies)]
+    kt = torch.from_numpy(k_np).to(dev)
+    lib = mla.library()
+    need = mla.top_k_renorm_workspace_size(w.rows, w.vocab)
+    tws = torch.empty(need, dtype=torch.uint8, device=dev)
+    import ctypes
+    sptr = ctypes.c_void_p(stream.cuda_stream)
+    targs = [(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(kt.data_ptr()), w.rows, w.vocab,
+              ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(tws.data_ptr()), need, sptr)
+             for a, b in zip(pin, pout)]
+
+    def tcall(i):
+        st = lib.mla_top_k_renorm_prob(*targs[i % copies])
+        if st != 0:
+            raise RuntimeError("mla_top_k_renorm_prob failed: %d" % st)
+    for i in range(copies):
+        tcall(i)
+    torch.cuda.synchronize()
+    chk = np.array([0, 1, 63, w.rows - 1])
+    want = oracle.top_k_renorm_prob(p_np[chk], k_np[chk])
+    for j in range(copies):
+        got = pout[j][torch.from_numpy(chk).to(dev)].cpu().numpy()
+        if not np.array_equal(got != 0, want != 0):
+            raise AssertionError(name + ": kept sets differ from the oracle")
+        m = want != 0
+        if np.max(np.abs(got[m] - want[m]) / want[m]) > 2e-6:
+            raise AssertionError(name + ": values differ from the oracle")
+    ms = event_times(torch, stream, tcall, 50)
+    ab = w.rows * w.vocab * 8 + w.rows * 4
+    us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
+    res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
+                 "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
+                 "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4), "input_copies": copies,
+                 "launches": 2}
+    log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
     return res
 
 

@@ -69,6 +69,10 @@ def library() -> ctypes.CDLL:
         lib.mla_decode_workspace_size.argtypes = [I, I, I, I, I]
         lib.mla_decode_num_splits.restype = I
         lib.mla_decode_num_splits.argtypes = [I, I, I, I, I, I]
+        lib.mla_top_k_renorm_prob.restype = I
+        lib.mla_top_k_renorm_prob.argtypes = [P, P, I, I, P, P, Z, P]
+        lib.mla_top_k_renorm_workspace_size.restype = Z
+        lib.mla_top_k_renorm_workspace_size.argtypes = [I, I]
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_status_string.argtypes = [I]
         lib.mla_version.restype = I
@@ -317,6 +321,47 @@ def cache_write(latent: torch.Tensor, kv_cache: torch.Tensor, slot_mapping: torc
                              kv_cache.numel() // HEAD_DIM_K, _stream(dev))
     _check("mla_cache_write", st)
     return kv_cache
+
+
+def top_k_renorm_workspace_size(rows: int, vocab: int) -> int:
+    return library().mla_top_k_renorm_workspace_size(rows, vocab)
+
+
+# Scratch for top_k_renorm_prob, one per (device, stream); it needs no initialisation.
+_topk_workspaces = {}
+
+
+def top_k_renorm_prob(probs: torch.Tensor, top_k: torch.Tensor, *,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Keep the top_k[r] largest entries of each row of probs [rows, vocab] fp32, zero the
+    rest and divide the kept ones by their sum (ties: the lower index first; k <= 0 or
+    k >= vocab keeps the whole row).  top_k: [rows] int32 on the same device.  ``out`` may
+    be ``probs`` (in place).  Returns out."""
+    lib = library()
+    if probs.dim() != 2 or probs.dtype != torch.float32 or not probs.is_contiguous():
+        raise TypeError("probs must be a contiguous [rows, vocab] float32 tensor")
+    dev = probs.device
+    rows, vocab = probs.shape
+    tk = _dev_i32(top_k, "top_k", dev)
+    if tk.numel() != rows:
+        raise TypeError("top_k must have one entry per row")
+    if out is None:
+        out = torch.empty_like(probs)
+    elif (out.shape != probs.shape or out.dtype != torch.float32 or out.device != dev
+          or not out.is_contiguous()):
+        raise TypeError("out must be a contiguous float32 tensor shaped like probs")
+    need = lib.mla_top_k_renorm_workspace_size(rows, vocab)
+    if workspace is None:
+        key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+        workspace = _topk_workspaces.get(key)
+        if workspace is None or workspace.numel() < need:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+            _topk_workspaces[key] = workspace
+    st = lib.mla_top_k_renorm_prob(_ptr(probs), _ptr(tk), rows, vocab, _ptr(out),
+                                   _ptr(workspace), workspace.numel(), _stream(dev))
+    _check("mla_top_k_renorm_prob", st)
+    return out
 
 
 def default_softmax_scale(qk_dim: int = 192) -> float:

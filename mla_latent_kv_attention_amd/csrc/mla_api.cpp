@@ -257,6 +257,31 @@ mla_status mla_cache_write(const void* latent, long N, const int32_t* slot_mappi
   return e == hipSuccess ? MLA_OK : MLA_E_LAUNCH;
 }
 
+namespace {
+constexpr int kTopKListMax = 2048;  // largest k served from per-chunk candidate lists
+}
+
+size_t mla_top_k_renorm_workspace_size(int rows, int vocab) {
+  if (rows <= 0 || vocab <= 0) return 0;
+  return (size_t)rows * (size_t)mla_impl::top_k_chunks(vocab) * kTopKListMax * 8;
+}
+
+mla_status mla_top_k_renorm_prob(const float* probs, const int32_t* top_k, int rows, int vocab,
+                                 float* out, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (rows < 0) return MLA_E_INVAL;
+  if (rows == 0) return MLA_OK;
+  if (vocab < 1) return MLA_E_INVAL;
+  if (!probs || !top_k || !out) return MLA_E_INVAL;
+  const size_t need = mla_top_k_renorm_workspace_size(rows, vocab);
+  if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 8 != 0)
+    return MLA_E_WORKSPACE;
+  const hipError_t e = mla_impl::launch_top_k_renorm(probs, top_k, rows, vocab, kTopKListMax,
+                                                     out, workspace,
+                                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? MLA_OK : MLA_E_LAUNCH;
+}
+
 mla_status mla_prefill(const void* q, const void* kv, int kv_dtype, float kv_scale,
                        const int32_t* cu_seqlens, int B, int T, int max_seqlen, int H,
                        float softmax_scale, void* out, int out_dtype, float* lse, void* stream) {

@@ -31,6 +31,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ["mla_decode", "mla_verify", "mla_prefill", "mla_merge_lse", "mla_cache_write",
+              "mla_top_k_renorm_prob", "mla_top_k_renorm_workspace_size",
               "mla_decode_workspace_size", "mla_decode_num_splits", "mla_status_string",
               "mla_version"]:
         assert n in names
@@ -112,6 +113,26 @@ def test_cache_write_rejects_bad_arguments(lib):
     assert lib.mla_cache_write(None, 4, P, P, 1, 0.01, 64, None) == -1
     assert lib.mla_cache_write(P, 4, None, P, 0, 1.0, 64, None) == -1
     assert lib.mla_cache_write(None, 0, None, None, 0, 1.0, 0, None) == 0
+
+
+def test_top_k_renorm_rejects_bad_arguments_and_sizes_its_workspace(lib):
+    P = ctypes.c_void_p(0x1000)
+    ws = lib.mla_top_k_renorm_workspace_size
+    # 16,384-entry chunks, 2,048 candidates of 8 bytes each per chunk
+    assert ws(128, 163840) == 128 * 10 * 2048 * 8
+    assert ws(3, 16385) == 3 * 2 * 2048 * 8
+    assert ws(0, 1000) == 0 and ws(4, 0) == 0
+    f = lib.mla_top_k_renorm_prob
+    need = ws(4, 1000)
+    assert f(P, P, -1, 1000, P, P, need, None) == -1
+    assert f(P, P, 4, 0, P, P, need, None) == -1
+    assert f(None, P, 4, 1000, P, P, need, None) == -1
+    assert f(P, None, 4, 1000, P, P, need, None) == -1
+    assert f(P, P, 4, 1000, None, P, need, None) == -1
+    assert f(P, P, 4, 1000, P, None, need, None) == -3
+    assert f(P, P, 4, 1000, P, P, need - 1, None) == -3
+    assert f(P, P, 4, 1000, P, ctypes.c_void_p(0x1004), need, None) == -3  # not 8-byte aligned
+    assert f(None, None, 0, 0, None, None, 0, None) == 0
 
 
 def test_prefill_rejects_bad_arguments(lib):
