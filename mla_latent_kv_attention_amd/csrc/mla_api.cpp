@@ -259,11 +259,18 @@ mla_status mla_cache_write(const void* latent, long N, const int32_t* slot_mappi
 
 namespace {
 constexpr int kTopKListMax = 2048;  // largest k served from per-chunk candidate lists
+
+// Workspace: candidate lists (8 bytes per entry, kTopKListMax per chunk), then one
+// float per chunk for the chunk sums of rows kept whole.
+size_t topk_list_bytes(int rows, int vocab) {
+  return align_up((size_t)rows * (size_t)mla_impl::top_k_chunks(vocab) * kTopKListMax * 8);
 }
+}  // namespace
 
 size_t mla_top_k_renorm_workspace_size(int rows, int vocab) {
   if (rows <= 0 || vocab <= 0) return 0;
-  return (size_t)rows * (size_t)mla_impl::top_k_chunks(vocab) * kTopKListMax * 8;
+  return topk_list_bytes(rows, vocab) +
+         align_up((size_t)rows * (size_t)mla_impl::top_k_chunks(vocab) * 4);
 }
 
 mla_status mla_top_k_renorm_prob(const float* probs, const int32_t* top_k, int rows, int vocab,
@@ -276,9 +283,11 @@ mla_status mla_top_k_renorm_prob(const float* probs, const int32_t* top_k, int r
   const size_t need = mla_top_k_renorm_workspace_size(rows, vocab);
   if (!workspace || workspace_bytes < need || (uintptr_t)workspace % 8 != 0)
     return MLA_E_WORKSPACE;
-  const hipError_t e = mla_impl::launch_top_k_renorm(probs, top_k, rows, vocab, kTopKListMax,
-                                                     out, workspace,
-                                                     static_cast<hipStream_t>(stream));
+  char* ws = static_cast<char*>(workspace);
+  const hipError_t e = mla_impl::launch_top_k_renorm(
+      probs, top_k, rows, vocab, kTopKListMax, out, ws,
+      reinterpret_cast<float*>(ws + topk_list_bytes(rows, vocab)),
+      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? MLA_OK : MLA_E_LAUNCH;
 }
 

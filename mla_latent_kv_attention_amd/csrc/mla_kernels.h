@@ -53,10 +53,12 @@ hipError_t launch_cache_write(const uint16_t* latent, long N, const int32_t* slo
                               bool kv_fp8, float kv_scale, long num_slots, hipStream_t stream);
 
 // Top-k renormalisation of rows x vocab fp32 probabilities (two launches).  The
-// list buffer holds rows * top_k_chunks(vocab) * list_max entries of 8 bytes.
+// list buffer holds rows * top_k_chunks(vocab) * list_max entries of 8 bytes, sums
+// rows * top_k_chunks(vocab) floats.
 long top_k_chunks(int vocab);
 hipError_t launch_top_k_renorm(const float* probs, const int32_t* top_k, int rows, int vocab,
-                               int list_max, float* out, void* list, hipStream_t stream);
+                               int list_max, float* out, void* list, float* sums,
+                               hipStream_t stream);
 
 struct PrefillParams {
   const uint16_t* q;           // [T, H, 576]

@@ -10,18 +10,21 @@
 // zero gives a zero row.
 //
 // The op is HBM-bound: read the row once, write it once.  Two launches:
-//  1. one 512-thread work-group per 16,384-entry chunk of a row holds its chunk
-//     in registers (32 entries per thread), finds the chunk's k-th largest entry
-//     by a radix select on order-preserving 32-bit keys (digits of 11, 11 and 10
-//     bits, counted in an LDS histogram), writes the chunk's k candidates (key,
-//     index) in index order to the workspace and zero-fills its output range.
-//     The row's top k are among the union of its chunks' top k.
-//  2. one 1024-thread work-group per row selects the row's k-th largest among
-//     its candidates the same way, resolves ties at the threshold by a second
-//     select on the index, sums the kept entries in a fixed order and writes
-//     p / sum over the kept positions.
-// For k above kListMax (or a chunk shorter than k) a chunk keeps no list: the
-// second launch reads that chunk's entries straight from the input.
+//  1. one 256-thread work-group per 8,192-entry chunk of a row holds the chunk
+//     in registers (32 entries per thread) and finds the chunk's k-th largest
+//     entry by a radix select on order-preserving 32-bit keys (digits of 11, 11
+//     and 10 bits counted in an LDS histogram).  The chunk's k candidates (key,
+//     index) go to the workspace in index order and its output range is
+//     zero-filled; the row's top k are among the union of its chunks' top k.
+//     For a row kept whole the work-group writes its chunk's sum instead.
+//  2. one 1024-thread work-group per row: for a row kept whole it writes p / S
+//     with S the sum of the chunk sums; otherwise it selects the row's k-th
+//     largest among the candidates the same way (from LDS when they fit),
+//     resolves ties at the threshold by a second select on the index, sums the
+//     kept entries in a fixed order and writes p / sum at the kept positions.
+// For k above the list limit (or a chunk not longer than k) a chunk keeps no
+// list and the second launch reads its entries straight from the input; rows
+// with such k are served by one work-group and run several times slower.
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -30,9 +33,10 @@ using namespace mla_dev;
 
 namespace {
 
-constexpr int kT1 = 512;                       // first-stage threads
+constexpr int kT1 = 256;                       // first-stage threads
 constexpr int kRounds = 8;                     // float4 loads per first-stage thread
-constexpr int kChunk = kRounds * 4 * kT1;      // 16,384 entries per chunk
+constexpr int kChunk = kRounds * 4 * kT1;      // 8,192 entries per chunk
+constexpr int kPack = kRounds / 2;             // per-round counts packed two to a word
 constexpr int kT2 = 1024;                      // second-stage threads
 constexpr int kHistBins = 2048;
 
@@ -73,29 +77,36 @@ __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, 
   return before + v;
 }
 
-// The same for four independent sums at once.  wsum holds 4 * NT / 64 words.
-template <int NT>
-__device__ __forceinline__ u32x4 block_incl_scan4(u32x4 v, uint32_t* wsum, u32x4* total) {
+// The same for W independent sums at once.  wsum holds W * NT / 64 words.
+template <int NT, int W>
+__device__ __forceinline__ void block_incl_scan_n(uint32_t (&v)[W], uint32_t* wsum,
+                                                  uint32_t (&total)[W]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    u32x4 t;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) t[q] = __shfl_up(v[q], o, 64);
-    if (lane >= o) v += t;
+    for (int q = 0; q < W; ++q) {
+      const uint32_t t = __shfl_up(v[q], o, 64);
+      if (lane >= o) v[q] += t;
+    }
   }
-  if (lane == 63) *(u32x4*)(wsum + 4 * wv) = v;
-  __syncthreads();
-  u32x4 before = {0u, 0u, 0u, 0u}, tot = {0u, 0u, 0u, 0u};
+  if (lane == 63)
 #pragma unroll
-  for (int i = 0; i < NT / 64; ++i) {
-    const u32x4 w = *(const u32x4*)(wsum + 4 * i);
-    if (i < wv) before += w;
-    tot += w;
+    for (int q = 0; q < W; ++q) wsum[W * wv + q] = v[q];
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < W; ++q) {
+    uint32_t before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
+      const uint32_t w = wsum[W * i + q];
+      before += (i < wv) ? w : 0u;
+      tot += w;
+    }
+    v[q] += before;
+    total[q] = tot;
   }
   __syncthreads();
-  *total = tot;
-  return before + v;
 }
 
 // Sum over the work-group in a fixed order (so the result is the same on every run).
@@ -136,6 +147,48 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, int nbins, uint
   __syncthreads();
 }
 
+// Radix select over the keys the threads feed through for_each(fn), for the rem
+// largest of them.  Returns T with *rem_eq and *count_eq such that the selected
+// keys are those > T plus rem_eq of the count_eq keys == T; when rem_eq ==
+// count_eq that is every key >= T.  The passes stop early once every key left in
+// the digit bin holding the rem-th largest is needed (then T is the bin's lowest
+// key).  Every thread calls it; 1 <= rem <= the number of keys.
+template <int NT, class ForEach>
+__device__ __forceinline__ uint32_t block_select(uint32_t rem, ForEach&& for_each,
+                                                 uint32_t* hist, uint32_t* wsum, uint32_t* sel,
+                                                 uint32_t* rem_eq, uint32_t* count_eq) {
+  uint32_t prefix = 0;
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = digit_shift(pass), nb = digit_bins(pass);
+    const int prev_shift = pass == 1 ? 21 : 10;
+    for (int i = threadIdx.x; i < kHistBins; i += NT) hist[i] = 0;
+    __syncthreads();
+    for_each([&](uint32_t kk) {
+      if (pass == 0 || (kk >> prev_shift) == prefix)
+        atomicAdd(&hist[(kk >> shift) & (uint32_t)(nb - 1)], 1u);
+    });
+    __syncthreads();
+    find_digit<NT>(hist, nb, rem, wsum, sel);
+    const uint32_t d = sel[0];
+    rem -= sel[1];
+    prefix = pass == 0 ? d : ((prefix << (pass == 1 ? 11 : 10)) | d);
+    const uint32_t in_bin = hist[d];
+    __syncthreads();
+    if (pass == 2) {
+      *count_eq = in_bin;
+      break;
+    }
+    if (in_bin == rem) {  // the whole bin is taken: keys >= its lowest key
+      *count_eq = 0;
+      rem = 0;
+      prefix <<= shift;
+      break;
+    }
+  }
+  *rem_eq = rem;
+  return prefix;
+}
+
 // The row's kept count: k <= 0 or k >= vocab keeps all of it.
 __device__ __forceinline__ int kept_count(int k, int vocab) {
   return (k <= 0 || k >= vocab) ? vocab : k;
@@ -146,23 +199,30 @@ __device__ __forceinline__ bool has_list(int keff, int len, int list_max) {
   return keff < len && keff <= list_max;
 }
 
+__device__ __forceinline__ int chunk_len(int vocab, int c) { return min(kChunk, vocab - c * kChunk); }
+
 template <bool kVec>
 __global__ __launch_bounds__(kT1) void topk_chunk_kernel(const float* __restrict__ probs,
                                                          const int32_t* __restrict__ top_k,
                                                          int vocab, int chunks, int list_max,
-                                                         float* out, u32x2* __restrict__ list) {
+                                                         float* out, u32x2* __restrict__ list,
+                                                         float* __restrict__ sums) {
   __shared__ uint32_t hist[kHistBins];
-  __shared__ __attribute__((aligned(16))) uint32_t wsum[4 * (kT1 / 64)];
+  __shared__ uint32_t wsum[kPack * (kT1 / 64)];
+  __shared__ float fsum[kT1 / 64];
   __shared__ uint32_t sel[2];
   const int row = blockIdx.x / chunks, c = blockIdx.x % chunks;
   const int t = threadIdx.x;
-  const int len = min(kChunk, vocab - c * kChunk);
-  const int keff = kept_count(top_k[row], vocab);
-  if (!has_list(keff, len, list_max)) return;  // the second stage reads this chunk itself
+  const int len = chunk_len(vocab, c);
   const float* src = probs + (size_t)row * vocab + (size_t)c * kChunk;
   float* dst = out + (size_t)row * vocab + (size_t)c * kChunk;
+  const int k_row = top_k[row];
 
-  // entry (j, e) of thread t is chunk entry 2048 j + 4 t + e
+  // entry (j, e) of thread t is chunk entry 4 (kT1 j + t) + e; the loads go out
+  // before k is tested (a chunk the second stage reads itself wastes them).
+  // Entries past the chunk's end get key 0, the lowest key: with k below the
+  // chunk's length they can never be selected (they also lose every tie, having
+  // the highest indices), so the selection needs no validity test.
   uint32_t key[kRounds][4];
 #pragma unroll
   for (int j = 0; j < kRounds; ++j) {
@@ -170,89 +230,75 @@ __global__ __launch_bounds__(kT1) void topk_chunk_kernel(const float* __restrict
     if constexpr (kVec) {
       const f32x4 v = (l < len) ? *(const f32x4*)(src + l) : (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) key[j][e] = rank_key(v[e]);
+      for (int e = 0; e < 4; ++e) key[j][e] = (l < len) ? rank_key(v[e]) : 0u;
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) key[j][e] = (l + e < len) ? rank_key(src[l + e]) : 0u;
     }
   }
   auto valid = [&](int j, int e) { return 4 * (kT1 * j + t) + e < len; };
+  const int keff = kept_count(k_row, vocab);
+  const bool keep_all = keff >= vocab;
+  if (!keep_all && !has_list(keff, len, list_max)) return;  // the second stage reads it
 
-  // ---- radix select of the keff-th largest key of the chunk ----
-  uint32_t prefix = 0, rem = (uint32_t)keff, count_eq = 0;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = digit_shift(pass), nb = digit_bins(pass);
-    const int prev_shift = pass == 1 ? 21 : 10;
-    for (int i = t; i < kHistBins; i += kT1) hist[i] = 0;
-    __syncthreads();
+  if (keep_all) {  // the whole row is kept: this chunk's share of the normaliser
+    float s = 0.f;
 #pragma unroll
     for (int j = 0; j < kRounds; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t kk = key[j][e];
-        if (valid(j, e) && (pass == 0 || (kk >> prev_shift) == prefix))
-          atomicAdd(&hist[(kk >> shift) & (uint32_t)(nb - 1)], 1u);
-      }
-    __syncthreads();
-    find_digit<kT1>(hist, nb, rem, wsum, sel);
-    const uint32_t d = sel[0];
-    rem -= sel[1];
-    prefix = pass == 0 ? d : ((prefix << (pass == 1 ? 11 : 10)) | d);
-    if (pass == 2) count_eq = hist[d];
-    __syncthreads();
+      for (int e = 0; e < 4; ++e) s += valid(j, e) ? key_value(key[j][e]) : 0.f;
+    const float S = block_sum_f32<kT1>(s, fsum);
+    if (t == 0) sums[(size_t)row * chunks + c] = S;
+    return;
   }
-  const uint32_t T = prefix, need_eq = rem;  // keep keys > T and the first need_eq keys == T
 
-  // ---- ranks of the ties (only when some of them are dropped) ----
-  // Per round counts are packed two to a word (each round holds at most 2048 entries).
-  bool cand[kRounds][4];
-  uint32_t tie_base[kRounds];
-  if (need_eq < count_eq) {
-    u32x4 packed = {0u, 0u, 0u, 0u};
+  // ---- the chunk's keff-th largest key T ----
+  uint32_t need_eq, count_eq;  // keys > T, and need_eq of the count_eq keys == T
+  const uint32_t T = block_select<kT1>(
+      (uint32_t)keff,
+      [&](auto&& fn) {
 #pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      uint32_t n = 0;
+        for (int j = 0; j < kRounds; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) n += (valid(j, e) && key[j][e] == T) ? 1u : 0u;
-      packed[j >> 1] += n << (16 * (j & 1));
-    }
-    u32x4 tot;
-    const u32x4 incl = block_incl_scan4<kT1>(packed, wsum, &tot);
-    uint32_t run = 0;  // ties in earlier rounds
+          for (int e = 0; e < 4; ++e)
+            fn(key[j][e]);
+      },
+      hist, wsum, sel, &need_eq, &count_eq);
+
+  // ---- the ties: when some are dropped, the need_eq of lowest index stay ----
+  uint32_t cut = 0xFFFFFFFFu;  // keep keys > T, and keys == T at local index <= cut
+  if (need_eq != count_eq) {
+    uint32_t r1, c1;  // local indices are unique: every selected ~index is >= the result
+    cut = ~block_select<kT1>(
+        need_eq,
+        [&](auto&& fn) {
 #pragma unroll
-    for (int j = 0; j < kRounds; ++j) {
-      const uint32_t mine = (packed[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      const uint32_t upto = (incl[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-      tie_base[j] = run + upto - mine;
-      run += (tot[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
-    }
-  } else {
+          for (int j = 0; j < kRounds; ++j)
 #pragma unroll
-    for (int j = 0; j < kRounds; ++j) tie_base[j] = 0;
+            for (int e = 0; e < 4; ++e)
+              if (key[j][e] == T) fn(~(uint32_t)(4 * (kT1 * j + t) + e));
+        },
+        hist, wsum, sel, &r1, &c1);
   }
+  // this thread's candidates as one bit per entry (bit 4 j + e): two registers
+  uint64_t cm = 0;
 #pragma unroll
-  for (int j = 0; j < kRounds; ++j) {
-    uint32_t r = tie_base[j];
+  for (int j = 0; j < kRounds; ++j)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t kk = key[j][e];
-      const bool tie = valid(j, e) && kk == T;
-      cand[j][e] = valid(j, e) && (kk > T || (tie && r < need_eq));
-      r += tie ? 1u : 0u;
+      if (kk > T || (kk == T && (uint32_t)(4 * (kT1 * j + t) + e) <= cut))
+        cm |= (uint64_t)1 << (4 * j + e);
     }
-  }
 
   // ---- write the candidates in index order, zero the chunk's output ----
-  u32x4 packed = {0u, 0u, 0u, 0u};
+  uint32_t packed[kPack] = {}, incl[kPack], tot[kPack];
 #pragma unroll
-  for (int j = 0; j < kRounds; ++j) {
-    uint32_t n = 0;
+  for (int j = 0; j < kRounds; ++j)
+    packed[j >> 1] += (uint32_t)__builtin_popcount((uint32_t)(cm >> (4 * j)) & 15u) << (16 * (j & 1));
 #pragma unroll
-    for (int e = 0; e < 4; ++e) n += cand[j][e] ? 1u : 0u;
-    packed[j >> 1] += n << (16 * (j & 1));
-  }
-  u32x4 tot;
-  const u32x4 incl = block_incl_scan4<kT1>(packed, wsum, &tot);
+  for (int q = 0; q < kPack; ++q) incl[q] = packed[q];
+  block_incl_scan_n<kT1, kPack>(incl, wsum, tot);
   u32x2* lst = list + ((size_t)row * chunks + c) * list_max;
   uint32_t run = 0;
 #pragma unroll
@@ -264,7 +310,7 @@ __global__ __launch_bounds__(kT1) void topk_chunk_kernel(const float* __restrict
     const int l = 4 * (kT1 * j + t);
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      if (cand[j][e]) {
+      if (((cm >> (4 * j + e)) & 1) && l + e < len) {  // (candidates lie inside the chunk)
         lst[pos] = (u32x2){key[j][e], (uint32_t)(c * kChunk + l + e)};
         ++pos;
       }
@@ -278,25 +324,52 @@ __global__ __launch_bounds__(kT1) void topk_chunk_kernel(const float* __restrict
   }
 }
 
+constexpr int kStage = 4096;  // candidates the second stage keeps in LDS
+
 template <bool kVec>
 __global__ __launch_bounds__(kT2) void topk_row_kernel(const float* probs,
                                                        const int32_t* __restrict__ top_k,
                                                        int vocab, int chunks, int list_max,
-                                                       float* out, const u32x2* __restrict__ list) {
+                                                       float* out, const u32x2* __restrict__ list,
+                                                       const float* __restrict__ sums) {
   __shared__ uint32_t hist[kHistBins];
   __shared__ uint32_t wsum[kT2 / 64];
   __shared__ float fsum[kT2 / 64];
   __shared__ uint32_t sel[2];
+  __shared__ uint32_t st_key[kStage];
+  __shared__ uint32_t st_idx[kStage];
   const int row = blockIdx.x;
   const int t = threadIdx.x;
   const int keff = kept_count(top_k[row], vocab);
   const float* src_row = probs + (size_t)row * vocab;
   float* dst_row = out + (size_t)row * vocab;
 
-  // Every candidate of the row once, as (key, index): a chunk's list, or the chunk itself.
-  auto for_each = [&](auto&& fn) {
+  if (keff >= vocab) {
+    // Whole row kept: p / S with S the sum of the first stage's chunk sums, in
+    // chunk order.
+    float S = 0.f;
+    for (int i = 0; i < chunks; ++i) S += sums[(size_t)row * chunks + i];
+    if constexpr (kVec) {
+#pragma unroll 4
+      for (int j = 4 * t; j < vocab; j += 4 * kT2) {
+        const f32x4 v = *(const f32x4*)(src_row + j);
+        f32x4 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (S != 0.f) ? __fdiv_rn(v[e], S) : 0.f;
+        *(f32x4*)(dst_row + j) = o;
+      }
+    } else {
+#pragma unroll 4
+      for (int j = t; j < vocab; j += kT2) dst_row[j] = (S != 0.f) ? __fdiv_rn(src_row[j], S) : 0.f;
+    }
+    return;
+  }
+
+  // Every candidate of the row once, in index order, as (key, index): a chunk's list,
+  // or the chunk itself.
+  auto for_each_global = [&](auto&& fn) {
     for (int c = 0; c < chunks; ++c) {
-      const int len = min(kChunk, vocab - c * kChunk);
+      const int len = chunk_len(vocab, c);
       if (has_list(keff, len, list_max)) {
         const u32x2* lst = list + ((size_t)row * chunks + c) * list_max;
         for (int j = t; j < keff; j += kT2) {
@@ -320,50 +393,75 @@ __global__ __launch_bounds__(kT2) void topk_row_kernel(const float* probs,
   };
   long n = 0;  // candidates in all
   for (int c = 0; c < chunks; ++c) {
-    const int len = min(kChunk, vocab - c * kChunk);
+    const int len = chunk_len(vocab, c);
     n += has_list(keff, len, list_max) ? keff : len;
   }
-
-  // Radix select of the rem-th largest of kf(key, idx) over the candidates that pass
-  // `keep`; returns it, leaves in *rem how many entries equal to it are to be taken
-  // and in *count_eq how many there are.
-  auto select = [&](uint32_t rem0, auto&& keep, auto&& kf, uint32_t* rem, uint32_t* count_eq) {
-    uint32_t prefix = 0, r = rem0;
-    for (int pass = 0; pass < 3; ++pass) {
-      const int shift = digit_shift(pass), nb = digit_bins(pass);
-      const int prev_shift = pass == 1 ? 21 : 10;
-      for (int i = t; i < kHistBins; i += kT2) hist[i] = 0;
-      __syncthreads();
-      for_each([&](uint32_t key, uint32_t idx) {
-        if (!keep(key, idx)) return;
-        const uint32_t kk = kf(key, idx);
-        if (pass == 0 || (kk >> prev_shift) == prefix)
-          atomicAdd(&hist[(kk >> shift) & (uint32_t)(nb - 1)], 1u);
-      });
-      __syncthreads();
-      find_digit<kT2>(hist, nb, r, wsum, sel);
-      const uint32_t d = sel[0];
-      r -= sel[1];
-      prefix = pass == 0 ? d : ((prefix << (pass == 1 ? 11 : 10)) | d);
-      if (pass == 2) *count_eq = hist[d];
-      __syncthreads();
+  // Few candidates (small k) are read into LDS once; the passes below then cost no
+  // global round trips.
+  const bool staged = n <= kStage;
+  if (staged) {
+    // entry q of the candidate sequence: chunk c at offset o_c, position q - o_c; the
+    // kStage / kT2 loads of a thread are issued together, then written to LDS
+    uint32_t sk[kStage / kT2], si[kStage / kT2];
+#pragma unroll
+    for (int u = 0; u < kStage / kT2; ++u) {
+      const int q = t + u * kT2;
+      sk[u] = 0;
+      si[u] = 0;
+      if (q >= n) continue;
+      int c = 0, o = 0;
+      for (;; ++c) {
+        const int len = chunk_len(vocab, c);
+        const int nc = has_list(keff, len, list_max) ? keff : len;
+        if (q < o + nc) break;
+        o += nc;
+      }
+      const int len = chunk_len(vocab, c);
+      if (has_list(keff, len, list_max)) {
+        const u32x2 e = list[((size_t)row * chunks + c) * list_max + (q - o)];
+        sk[u] = e.x;
+        si[u] = e.y;
+      } else {
+        si[u] = (uint32_t)(c * kChunk + (q - o));
+        sk[u] = rank_key(src_row[si[u]]);
+      }
     }
-    *rem = r;
-    return prefix;
+#pragma unroll
+    for (int u = 0; u < kStage / kT2; ++u) {
+      const int q = t + u * kT2;
+      if (q < n) {
+        st_key[q] = sk[u];
+        st_idx[q] = si[u];
+      }
+    }
+    __syncthreads();
+  }
+  auto for_each = [&](auto&& fn) {
+    if (staged) {
+      for (int i = t; i < (int)n; i += kT2) fn(st_key[i], st_idx[i]);
+    } else {
+      for_each_global(fn);
+    }
   };
 
   // kept: key > T, or key == T and index <= cut
   uint32_t T = 0, cut = 0xFFFFFFFFu;
-  bool all = n <= keff;
+  const bool all = n <= keff;
   if (!all) {
     uint32_t need_eq, count_eq;
-    T = select((uint32_t)keff, [](uint32_t, uint32_t) { return true; },
-               [](uint32_t key, uint32_t) { return key; }, &need_eq, &count_eq);
-    if (need_eq < count_eq) {  // the need_eq tied entries of lowest index
-      uint32_t r1, c1;
-      const uint32_t T_ = T;
-      cut = ~select(need_eq, [T_](uint32_t key, uint32_t) { return key == T_; },
-                    [](uint32_t, uint32_t idx) { return ~idx; }, &r1, &c1);
+    T = block_select<kT2>(
+        (uint32_t)keff, [&](auto&& fn) { for_each([&](uint32_t key, uint32_t) { fn(key); }); },
+        hist, wsum, sel, &need_eq, &count_eq);
+    if (need_eq != count_eq) {  // the need_eq tied entries of lowest index
+      uint32_t r1, c1;  // indices are unique: every selected ~index is >= the result
+      cut = ~block_select<kT2>(
+          need_eq,
+          [&](auto&& fn) {
+            for_each([&](uint32_t key, uint32_t idx) {
+              if (key == T) fn(~idx);
+            });
+          },
+          hist, wsum, sel, &r1, &c1);
     }
   }
   auto kept = [&](uint32_t key, uint32_t idx) {
@@ -375,23 +473,34 @@ __global__ __launch_bounds__(kT2) void topk_row_kernel(const float* probs,
     if (kept(key, idx)) s += key_value(key);
   });
   const float S = block_sum_f32<kT2>(s, fsum);
+  auto scaled = [&](float v) { return (S != 0.f) ? __fdiv_rn(v, S) : 0.f; };
 
+  if (staged) {
+    // a listed chunk was zeroed by the first stage: only its kept entries are written
+    for (int i = t; i < (int)n; i += kT2) {
+      const uint32_t key = st_key[i], idx = st_idx[i];
+      const bool listed = has_list(keff, chunk_len(vocab, (int)(idx / kChunk)), list_max);
+      if (kept(key, idx))
+        dst_row[idx] = scaled(key_value(key));
+      else if (!listed)
+        dst_row[idx] = 0.f;
+    }
+    return;
+  }
   for (int c = 0; c < chunks; ++c) {
-    const int len = min(kChunk, vocab - c * kChunk);
+    const int len = chunk_len(vocab, c);
     if (has_list(keff, len, list_max)) {
-      // the first launch zeroed the chunk; only the kept candidates are written
       const u32x2* lst = list + ((size_t)row * chunks + c) * list_max;
       for (int j = t; j < keff; j += kT2) {
         const u32x2 e = lst[j];
-        if (kept(e.x, e.y)) dst_row[e.y] = (S != 0.f) ? __fdiv_rn(key_value(e.x), S) : 0.f;
+        if (kept(e.x, e.y)) dst_row[e.y] = scaled(key_value(e.x));
       }
     } else {
       const float* src = src_row + (size_t)c * kChunk;
       float* dst = dst_row + (size_t)c * kChunk;
       for (int j = t; j < len; j += kT2) {
         const float v = src[j];
-        const bool k_ = kept(rank_key(v), (uint32_t)(c * kChunk + j));
-        dst[j] = (k_ && S != 0.f) ? __fdiv_rn(v, S) : 0.f;
+        dst[j] = kept(rank_key(v), (uint32_t)(c * kChunk + j)) ? scaled(v) : 0.f;
       }
     }
   }
@@ -402,23 +511,26 @@ __global__ __launch_bounds__(kT2) void topk_row_kernel(const float* probs,
 long top_k_chunks(int vocab) { return vocab > 0 ? (vocab + kChunk - 1) / kChunk : 0; }
 
 hipError_t launch_top_k_renorm(const float* probs, const int32_t* top_k, int rows, int vocab,
-                               int list_max, float* out, void* list, hipStream_t stream) {
+                               int list_max, float* out, void* list, float* sums,
+                               hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   const long chunks = top_k_chunks(vocab);
-  const long g1 = rows * chunks;
-  if (g1 > 0x7fffffffL) return hipErrorInvalidValue;
+  const long grid = rows * chunks;
+  if (grid > 0x7fffffffL) return hipErrorInvalidValue;
   const bool vec = (vocab % 4 == 0) && ((uintptr_t)probs % 16 == 0) && ((uintptr_t)out % 16 == 0);
   u32x2* l = (u32x2*)list;
   if (vec) {
-    hipLaunchKernelGGL(topk_chunk_kernel<true>, dim3((unsigned)g1), dim3(kT1), 0, stream, probs,
-                       top_k, vocab, (int)chunks, list_max, out, l);
-    hipLaunchKernelGGL(topk_row_kernel<true>, dim3(rows), dim3(kT2), 0, stream, probs, top_k,
-                       vocab, (int)chunks, list_max, out, (const u32x2*)l);
+    hipLaunchKernelGGL(topk_chunk_kernel<true>, dim3((unsigned)grid), dim3(kT1), 0, stream, probs,
+                       top_k, vocab, (int)chunks, list_max, out, l, sums);
+    hipLaunchKernelGGL(topk_row_kernel<true>, dim3(rows), dim3(kT2), 0, stream, probs,
+                       top_k, vocab, (int)chunks, list_max, out, (const u32x2*)l,
+                       (const float*)sums);
   } else {
-    hipLaunchKernelGGL(topk_chunk_kernel<false>, dim3((unsigned)g1), dim3(kT1), 0, stream, probs,
-                       top_k, vocab, (int)chunks, list_max, out, l);
-    hipLaunchKernelGGL(topk_row_kernel<false>, dim3(rows), dim3(kT2), 0, stream, probs, top_k,
-                       vocab, (int)chunks, list_max, out, (const u32x2*)l);
+    hipLaunchKernelGGL(topk_chunk_kernel<false>, dim3((unsigned)grid), dim3(kT1), 0, stream,
+                       probs, top_k, vocab, (int)chunks, list_max, out, l, sums);
+    hipLaunchKernelGGL(topk_row_kernel<false>, dim3(rows), dim3(kT2), 0, stream, probs,
+                       top_k, vocab, (int)chunks, list_max, out, (const u32x2*)l,
+                       (const float*)sums);
   }
   return hipGetLastError();
 }

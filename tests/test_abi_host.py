@@ -118,9 +118,11 @@ def test_cache_write_rejects_bad_arguments(lib):
 def test_top_k_renorm_rejects_bad_arguments_and_sizes_its_workspace(lib):
     P = ctypes.c_void_p(0x1000)
     ws = lib.mla_top_k_renorm_workspace_size
-    # 16,384-entry chunks, 2,048 candidates of 8 bytes each per chunk
-    assert ws(128, 163840) == 128 * 10 * 2048 * 8
-    assert ws(3, 16385) == 3 * 2 * 2048 * 8
+    # 8,192-entry chunks, 2,048 candidates of 8 bytes each per chunk, then one float
+    # per chunk; both parts 256-byte aligned
+    up = lambda x: (x + 255) // 256 * 256
+    assert ws(128, 163840) == up(128 * 20 * 2048 * 8) + up(128 * 20 * 4)
+    assert ws(3, 16385) == up(3 * 3 * 2048 * 8) + up(3 * 3 * 4)
     assert ws(0, 1000) == 0 and ws(4, 0) == 0
     f = lib.mla_top_k_renorm_prob
     need = ws(4, 1000)

@@ -7,7 +7,7 @@ takes (each of 1,024 threads adds at most ceil(n / 1,024) terms in order, then a
 fixed tree over 1,024 partial sums; non-negative terms): relative error at most
 (ceil(n / 1024) + 12) * 2^-24, one more ulp for the division.
 
-Cases span several 16,384-entry chunks and a ragged last chunk, the vectorised
+Cases span several 8,192-entry chunks and a ragged last chunk, the vectorised
 (vocab % 4 == 0) and scalar loads, k around the 2,048 list limit (above it the
 second stage reads the row itself), ties at the k-th value inside a chunk and
 across chunks, keep-all values of k, zero rows, vocab 1, in-place calls,
@@ -57,7 +57,7 @@ def check(got, p, ks):
         assert rel.size == 0 or rel.max() <= tol, (r, k, float(rel.max()), tol)
 
 
-KS = [1, 2, 7, 100, 2047, 2048, 2049, 16383, 16384, 16385, 30000, 0, -3]
+KS = [1, 2, 7, 100, 400, 512, 513, 2047, 2048, 2049, 8191, 8192, 8193, 16384, 30000, 0, -3]
 
 
 @pytest.mark.parametrize("vocab", [3 * 16384 + 1234, 3 * 16384 + 1236, 40000, 100, 16384])
