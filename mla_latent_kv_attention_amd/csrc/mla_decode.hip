@@ -128,10 +128,11 @@ __device__ __forceinline__ float sum16(float v) {
 }
 
 // Last piece of sequence b: combine the partials of pieces w_first..w_last for
-// row rr (16 threads per row, 4 dims each per 64-dim slab).  The lse of all pieces
-// are read in parallel (one piece per lane), the partial rows four pieces at a
-// time; a piece that saw no key of the row has lse = -inf and an unwritten row,
-// which its zero weight selects away.
+// row rr (16 threads per row, 4 dims each per 64-dim slab).  The pieces are taken
+// four at a time, each batch's lse values loaded together with its partial rows,
+// and combined online against a running maximum (one global round trip per batch,
+// none for a separate pass over the lse values).  A piece that saw no key of the
+// row has lse = -inf and an unwritten row, which its zero weight selects away.
 __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int b, int rr, size_t n,
                                              int w_first, int w_last) {
   const int j = threadIdx.x & 15;
@@ -139,39 +140,38 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int b, int r
   const float* lse_b = p.part_lse + (size_t)b * R + rr;  // slot v at v * R
   // slot v's rows start at part_out + (v + b) * R * 512; this lane's bytes within it
   const uint32_t off = (uint32_t)(rr * kDV + 4 * j) * 4;
-  float mx = -INFINITY;
-  for (int v = w_first + j; v <= w_last; v += 16) mx = fmaxf(mx, load_agent(lse_b + v * R));
-  mx = max16(mx);
+  float mx = -INFINITY, ls = 0.f;
   f32x4 o8[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) o8[k] = (f32x4){0.f, 0.f, 0.f, 0.f};
-  float ls = 0.f;
+  for (int v0 = w_first; v0 <= w_last; v0 += 4) {
+    float l4[4];
+    f32x4 x[4][8];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int v = min(v0 + u, w_last);  // past the end: re-read the last slot, weight 0
+      l4[u] = (v0 + u <= w_last) ? load_agent(lse_b + v * R) : -INFINITY;
+      const auto rsrc = agent_rsrc(p.part_out + (size_t)(v + b) * R * kDV);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[u][k] = load_agent16(rsrc, off + 256 * k);
+    }
+    const float m_new = fmaxf(fmaxf(mx, fmaxf(l4[0], l4[1])), fmaxf(l4[2], l4[3]));
+    if (m_new == -INFINITY) continue;  // nothing seen yet
+    const float r = (mx == -INFINITY) ? 0.f : expf(mx - m_new);
+    ls *= r;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) o8[k] *= r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wt = (l4[u] == -INFINITY) ? 0.f : expf(l4[u] - m_new);
+      ls += wt;
+      if (wt > 0.f)
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o8[k] += wt * x[u][k];
+    }
+    mx = m_new;
+  }
   if (mx != -INFINITY) {
-    for (int v = w_first + j; v <= w_last; v += 16) {
-      const float x = load_agent(lse_b + v * R);
-      ls += (x == -INFINITY) ? 0.f : expf(x - mx);
-    }
-    ls = sum16(ls);
-    for (int v0 = w_first; v0 <= w_last; v0 += 4) {
-      float wt[4];
-      f32x4 x[4][8];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = min(v0 + u, w_last);  // past the end: re-read the last slot, weight 0
-        const float l = load_agent(lse_b + v * R);
-        wt[u] = (v0 + u <= w_last && l != -INFINITY) ? expf(l - mx) : 0.f;
-        const auto rsrc = agent_rsrc(p.part_out + (size_t)(v + b) * R * kDV);
-#pragma unroll
-        for (int k = 0; k < 8; ++k) x[u][k] = load_agent16(rsrc, off + 256 * k);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const f32x4 t = wt[u] * x[u][k];
-          if (wt[u] > 0.f) o8[k] += t;
-        }
-    }
     const float il = 1.f / ls;
 #pragma unroll
     for (int k = 0; k < 8; ++k) o8[k] *= il;
@@ -595,15 +595,15 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
 }
 
 // The merge of sequences split into many shares, as a launch of its own: one
-// 256-thread work-group per output row.  The shares' lse are reduced across the
-// work-group; then 8 groups of 32 threads take every 8th share (each thread 16 of
-// the 512 dims) so that many shares are in flight at once, and the groups' sums
-// meet in LDS.  A share that saw no key of the row has lse = -inf and an unwritten
-// row, which its zero weight selects away.
+// 256-thread work-group per output row.  8 groups of 32 threads take every 8th
+// share (each thread 16 of the 512 dims), four shares' loads in flight at a time,
+// each group combining its shares online against a running maximum; the groups'
+// results meet in LDS.  The decode launch that wrote the shares has completed, so
+// plain loads see them.  A share that saw no key of the row has lse = -inf and an
+// unwritten row, which its zero weight selects away.
 __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p) {
   __shared__ float red[8][kDV + 4];
-  __shared__ float wred[8];
-  __shared__ float mred[4];
+  __shared__ float gm[8], gl[8];
   const int tid = threadIdx.x;
   const size_t n = blockIdx.x;
   const int b = (int)(n / p.R), rr = (int)(n % p.R);
@@ -611,56 +611,60 @@ __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p)
   if (w_first == w_last) return;  // one piece held the whole sequence and wrote it
   const size_t R = p.R;
   const float* lse_b = p.part_lse + (size_t)b * R + rr;  // share v at v * R
-  float mx = -INFINITY;
-  for (int v = w_first + tid; v <= w_last; v += 256) mx = fmaxf(mx, load_agent(lse_b + v * R));
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if ((tid & 63) == 0) mred[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
   const int g = tid >> 5, l = tid & 31;
   f32x4 o4[4] = {};
-  float ws = 0.f;
-  if (mx != -INFINITY) {
-    const uint32_t off = (uint32_t)(rr * kDV + 16 * l) * 4;
-    // four of the group's shares per iteration, all their loads in flight together
-    for (int v0 = w_first + g; v0 <= w_last; v0 += 32) {
-      float wt[4];
-      f32x4 t[4][4];
+  float mx = -INFINITY, ls = 0.f;
+  for (int v0 = w_first + g; v0 <= w_last; v0 += 32) {
+    float l4[4];
+    f32x4 t[4][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int v = min(v0 + 8 * u, w_last);  // past the end: re-read, weight 0
-        const float x = load_agent(lse_b + v * R);
-        wt[u] = (v0 + 8 * u <= w_last && x != -INFINITY) ? expf(x - mx) : 0.f;
-        const auto rsrc = agent_rsrc(p.part_out + (size_t)(v + b) * R * kDV);
+    for (int u = 0; u < 4; ++u) {
+      const int v = min(v0 + 8 * u, w_last);  // past the end: re-read, weight 0
+      l4[u] = (v0 + 8 * u <= w_last) ? lse_b[v * R] : -INFINITY;
+      const f32x4* src = (const f32x4*)(p.part_out + ((size_t)(v + b) * R + rr) * kDV + 16 * l);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) t[u][k] = load_agent16(rsrc, off + 16 * k);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        ws += wt[u];
-        if (wt[u] > 0.f) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) o4[k] += wt[u] * t[u][k];
-        }
-      }
+      for (int k = 0; k < 4; ++k) t[u][k] = src[k];
     }
+    const float m_new = fmaxf(fmaxf(mx, fmaxf(l4[0], l4[1])), fmaxf(l4[2], l4[3]));
+    if (m_new == -INFINITY) continue;
+    const float r = (mx == -INFINITY) ? 0.f : expf(mx - m_new);
+    ls *= r;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o4[k] *= r;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float wt = (l4[u] == -INFINITY) ? 0.f : expf(l4[u] - m_new);
+      ls += wt;
+      if (wt > 0.f)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o4[k] += wt * t[u][k];
+    }
+    mx = m_new;
   }
 #pragma unroll
   for (int k = 0; k < 4; ++k) *(f32x4*)&red[g][16 * l + 4 * k] = o4[k];
-  if (l == 0) wred[g] = ws;
+  if (l == 0) {
+    gm[g] = mx;
+    gl[g] = ls;
+  }
   __syncthreads();
-  float wsum = 0.f;
+  float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) wsum += wred[i];
+  for (int i = 0; i < 8; ++i) M = fmaxf(M, gm[i]);
+  float sc[8], wsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    sc[i] = (gm[i] == -INFINITY) ? 0.f : expf(gm[i] - M);
+    wsum += gl[i] * sc[i];
+  }
   // thread tid writes dims 2 tid, 2 tid + 1
   float2 v2 = {0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    v2.x += red[i][2 * tid];
-    v2.y += red[i][2 * tid + 1];
+    v2.x += red[i][2 * tid] * sc[i];
+    v2.y += red[i][2 * tid + 1] * sc[i];
   }
-  const float il = (mx != -INFINITY && wsum > 0.f) ? 1.f / wsum : 0.f;
+  const float il = (M != -INFINITY && wsum > 0.f) ? 1.f / wsum : 0.f;
   v2.x *= il;
   v2.y *= il;
   if (p.out_bf16) {
@@ -669,7 +673,7 @@ __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p)
   } else {
     *(float2*)((float*)p.out + n * kDV + 2 * tid) = v2;
   }
-  if (p.lse && tid == 0) p.lse[n] = (mx == -INFINITY) ? -INFINITY : mx + logf(wsum);
+  if (p.lse && tid == 0) p.lse[n] = (M == -INFINITY) ? -INFINITY : M + logf(wsum);
 }
 
 // One work-group of 128 threads per row; each thread owns 4 of the 512 dims.  The
