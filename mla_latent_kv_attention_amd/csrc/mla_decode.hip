@@ -108,11 +108,18 @@ __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
   return r;
 }
 
+// a / b for non-negative a, b > 0: 32-bit when both fit (the usual case), which
+// is far shorter than the 64-bit division sequence.
+__device__ __forceinline__ long div_nonneg(long a, long b) {
+  if (((unsigned long)(a | b) >> 32) == 0) return (long)((uint32_t)a / (uint32_t)b);
+  return a / b;
+}
+
 // Work-group w of W owns steps [first_step(w), first_step(w + 1)) of the batch's
 // concatenated step list; step s belongs to owner(s).
-__device__ __forceinline__ long first_step(long w, long N, int W) { return w * N / W; }
+__device__ __forceinline__ long first_step(long w, long N, int W) { return div_nonneg(w * N, W); }
 __device__ __forceinline__ int owner(long s, long N, int W) {
-  return (int)(((s + 1) * W - 1) / N);
+  return (int)div_nonneg((s + 1) * W - 1, N);
 }
 
 // Max / sum over the 16 lanes of a row group (lanes 16 g .. 16 g + 15).
@@ -241,47 +248,89 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
   // Piece 0 also writes the rows of sequences without visible keys: zeros and
   // lse = -inf.
   __shared__ long long red[kWaves];
-  __shared__ long long seg[2];  // first sequence of the piece, its offset in the list
+  __shared__ long long seg[3];  // first sequence of the piece, its list offset, list length
+  __shared__ int seg_range[4];  // L, lo, hi, n of that first sequence
   const int c = p.seg_steps;
-  long long part = 0;
-  for (int b0 = 0; b0 < p.B; b0 += 256) {
-    const int b = b0 + tid;
-    if (b >= p.B) break;
-    const int nb = seq_range(p, b).n;
-    part += nb > 0 ? nb + c : 0;
-    if (w == 0 && nb == 0 && !p.merge_in_kernel && rb == 0) {
+  // the sequences without keys: piece 0 writes their rows (and, for the separate
+  // merge, an empty share range)
+  auto write_empty = [&](int b) {
+    if (!p.merge_in_kernel && rb == 0) {
       p.seq_pieces[2 * b] = 0;  // no shares to merge
       p.seq_pieces[2 * b + 1] = 0;
     }
-    if (w == 0 && nb == 0) {
-      for (int row = 0; row < 16; ++row) {
-        const int rr = rb * 16 + row;
-        if (rr >= p.R) break;
-        const size_t n = (size_t)b * p.R + rr;
-        for (int d = 0; d < kDV; d += 4) store_row4(p, n, d, (f32x4){0.f, 0.f, 0.f, 0.f});
-        if (p.lse) p.lse[n] = -INFINITY;
+    for (int row = 0; row < 16; ++row) {
+      const int rr = rb * 16 + row;
+      if (rr >= p.R) break;
+      const size_t n = (size_t)b * p.R + rr;
+      for (int d = 0; d < kDV; d += 4) store_row4(p, n, d, (f32x4){0.f, 0.f, 0.f, 0.f});
+      if (p.lse) p.lse[n] = -INFINITY;
+    }
+  };
+  long long N;
+  if (p.B <= 64) {
+    // One wave holds every sequence (one per lane): its sum, its scan and the search
+    // for this piece's first sequence need no work-group barrier but the last.
+    if (wave == 0) {
+      const int b = lane;
+      SeqRange sr = {0, 0, 0, 0, 0};
+      if (b < p.B) sr = seq_range(p, b);
+      const long long mb = sr.n > 0 ? sr.n + c : 0;
+      if (w == 0 && b < p.B && sr.n == 0) write_empty(b);
+      long long incl = mb;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const long long t = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += t;
+      }
+      const long long tot = __shfl(incl, 63, 64);
+      const int We0 = (int)min((long long)W, tot);
+      const long S0_ = w < We0 ? first_step(w, tot, We0) : 0;
+      if (lane == 0) seg[2] = tot;
+      if (w < We0 && mb > 0 && incl - mb <= S0_ && S0_ < incl) {
+        seg[0] = b;
+        seg[1] = incl - mb;
+        seg_range[0] = sr.L;
+        seg_range[1] = sr.lo;
+        seg_range[2] = sr.hi;
+        seg_range[3] = sr.n;
       }
     }
+    __syncthreads();
+    N = seg[2];
+  } else {
+    long long part = 0;
+    for (int b0 = 0; b0 < p.B; b0 += 256) {
+      const int b = b0 + tid;
+      if (b >= p.B) break;
+      const int nb = seq_range(p, b).n;
+      part += nb > 0 ? nb + c : 0;
+      if (w == 0 && nb == 0) write_empty(b);
+    }
+    if (tid == 0) seg[0] = p.B;
+    N = block_sum(part, red);
   }
-  if (tid == 0) seg[0] = p.B;
-  const long long N = block_sum(part, red);
   // With fewer list entries than pieces only the first N pieces take part, so every
   // piece in use holds at least one entry: the pieces that share a sequence's real
   // steps are consecutive and each holds some of them.
   const int We = (int)min((long long)W, N);
   if (w >= We) return;
   const long S0 = first_step(w, N, We), S1 = first_step(w + 1, N, We);
-  {
+  if (p.B > 64) {
     long long carry = 0;
     for (int b0 = 0; b0 < p.B; b0 += 256) {
       const int b = b0 + tid;
-      const int nb = b < p.B ? seq_range(p, b).n : 0;
-      const long long mb = nb > 0 ? nb + c : 0;
+      SeqRange sr = {0, 0, 0, 0, 0};
+      if (b < p.B) sr = seq_range(p, b);
+      const long long mb = sr.n > 0 ? sr.n + c : 0;
       long long tot;
       const long long ob = carry + block_exclusive_scan(mb, red, &tot);
       if (mb > 0 && ob <= S0 && S0 < ob + mb) {  // the one sequence holding entry S0
         seg[0] = b;
         seg[1] = ob;
+        seg_range[0] = sr.L;
+        seg_range[1] = sr.lo;
+        seg_range[2] = sr.hi;
+        seg_range[3] = sr.n;
       }
       carry += tot;
       __syncthreads();
@@ -292,7 +341,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
   long o = (long)seg[1];  // list offset of sequence b
 
   for (int b = b_first; b < p.B && o < S1; ++b) {
-    const SeqRange sr = seq_range(p, b);
+    // the first sequence's range came with the scan; later ones are read here
+    SeqRange sr;
+    if (b == b_first) {
+      sr.L = seg_range[0];
+      sr.lo = seg_range[1];
+      sr.hi = seg_range[2];
+      sr.n = seg_range[3];
+      sr.base = sr.lo & ~(kStep - 1);
+    } else {
+      sr = seq_range(p, b);
+    }
     if (sr.n == 0) continue;  // empty sequences were written above
     const long rs = o + c;    // list offset of b's first real step
     o = rs + sr.n;
@@ -308,7 +367,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
       p.seq_pieces[2 * b + 1] = w_last;
     }
 
-    __syncthreads();  // the previous segment is done with the LDS tiles
+    if (b != b_first) __syncthreads();  // the previous segment is done with the LDS tiles
     // The 18 Q^T fragments (B operand of the score MFMA) of the lane's query row stay
     // in registers for the whole segment, loaded straight from global memory before
     // the key prefetch: only MFMAs read them, so they can live in accumulation
