@@ -78,18 +78,22 @@ def cpu_baseline(q, cache, alg_bytes, min_seconds=10.0, max_reps=400):
 
 
 def gpu_clocks():
-    """Current shader / memory clocks as the SMI tool reports them (text), or None."""
-    import subprocess
-    for cmd in (["amd-smi", "metric", "--clock"], ["rocm-smi", "--showclocks"]):
-        try:
-            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
-        except (OSError, subprocess.TimeoutExpired):
-            continue
-        if r.returncode == 0 and r.stdout.strip():
-            lines = [l.strip() for l in r.stdout.splitlines()
-                     if any(k in l.upper() for k in ("SCLK", "MCLK", "GFX_0", "MEM_0", "CLK"))]
-            return " | ".join(lines[:12]) or None
-    return None
+    """Current shader / memory clock levels from the amdgpu sysfs files (the level
+    marked '*'), or None.  Plain file reads: this process has the GPU open, so it must
+    not start other programs."""
+    import glob
+    found = []
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    cur = [l.strip() for l in f if "*" in l]
+            except OSError:
+                continue
+            if cur:
+                found.append("%s %s: %s" % (os.path.basename(os.path.dirname(dev)), name,
+                                            cur[0]))
+    return " | ".join(found[:8]) or None
 
 
 def event_times(torch, stream, fn, n):
@@ -137,12 +141,15 @@ def graph_replay_us(torch, fns, out, calls=100, replays=5):
 
 
 def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device, check_out,
-                      check_lse, dev, stream):
+                      check_lse, dev, stream, only=None):
     """The other decode / verify configurations: parity on sampled rows, then per-call
     HIP-event times (p10 / p50 / p90) and, for the launch-bound ones, HIP-graph replays."""
     res = {}
+    want = lambda n: only is None or n in only
     for name, rotate in (("decode_b1_h12_l1024_bf16", 1), ("verify_b4_p4_h12_l32768_bf16", 4),
                          ("verify_b1_p4_h12_l32768_fp8", 28)):
+        if not want(name):
+            continue
         w = mi.WORKLOADS[name]
         log("generating", name)
         d = mi.decode_inputs(w)
@@ -183,131 +190,134 @@ def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device,
                                                           res[name]["gbs_p50"]))
         del pools, kv0, fns
 
-    # 142,000-token contexts in 8 contiguous partitions (one call each, as a position shard
-    # would compute its share) merged by mla_merge_lse
-    name = "decode_b8_h12_l142000_fp8_8parts"
-    w = mi.WORKLOADS[name]
-    log("generating", name)
-    d = mi.decode_inputs(w)
-    q_np, cache = d["q"], d["cache"]
-    B, P, H = q_np.shape[:3]
-    N = B * P * H
-    kv, bt, sl = cache_to_device(cache, dev)
-    q = bf16_tensor(q_np, dev).reshape(B, P, H, 576)
-    bounds = mi.partition_bounds(int(cache.seq_lens[0]), w.partitions)
-    S = len(bounds)
-    part_out = torch.empty((S, B, P, H, 512), dtype=torch.float32, device=dev)
-    part_lse = torch.empty((S, B, P, H), dtype=torch.float32, device=dev)
-    out = torch.empty((N, 512), dtype=torch.float32, device=dev)
-    lse = torch.empty((N,), dtype=torch.float32, device=dev)
-    span = max(hi - lo for lo, hi in bounds)
-    wss = [torch.zeros(max(1, mla.decode_workspace_size(B, P, H, span)), dtype=torch.uint8,
-                       device=dev) for _ in bounds]
-    kbs = [torch.full((B,), lo, dtype=torch.int32, device=dev) for lo, _ in bounds]
-    kes = [torch.full((B,), hi, dtype=torch.int32, device=dev) for _, hi in bounds]
-    fns = [mla.verify_launcher(q, kv, bt, sl, softmax_scale=w.softmax_scale,
-                               kv_scale=cache.kv_scale, max_kv_len=span, out=part_out[j],
-                               lse=part_lse[j], workspace=wss[j], kv_begin=kbs[j], kv_end=kes[j])
-           for j in range(S)]
+    if want("decode_b8_h12_l142000_fp8_8parts"):
+        # 142,000-token contexts in 8 contiguous partitions (one call each, as a position shard
+        # would compute its share) merged by mla_merge_lse
+        name = "decode_b8_h12_l142000_fp8_8parts"
+        w = mi.WORKLOADS[name]
+        log("generating", name)
+        d = mi.decode_inputs(w)
+        q_np, cache = d["q"], d["cache"]
+        B, P, H = q_np.shape[:3]
+        N = B * P * H
+        kv, bt, sl = cache_to_device(cache, dev)
+        q = bf16_tensor(q_np, dev).reshape(B, P, H, 576)
+        bounds = mi.partition_bounds(int(cache.seq_lens[0]), w.partitions)
+        S = len(bounds)
+        part_out = torch.empty((S, B, P, H, 512), dtype=torch.float32, device=dev)
+        part_lse = torch.empty((S, B, P, H), dtype=torch.float32, device=dev)
+        out = torch.empty((N, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((N,), dtype=torch.float32, device=dev)
+        span = max(hi - lo for lo, hi in bounds)
+        wss = [torch.zeros(max(1, mla.decode_workspace_size(B, P, H, span)), dtype=torch.uint8,
+                           device=dev) for _ in bounds]
+        kbs = [torch.full((B,), lo, dtype=torch.int32, device=dev) for lo, _ in bounds]
+        kes = [torch.full((B,), hi, dtype=torch.int32, device=dev) for _, hi in bounds]
+        fns = [mla.verify_launcher(q, kv, bt, sl, softmax_scale=w.softmax_scale,
+                                   kv_scale=cache.kv_scale, max_kv_len=span, out=part_out[j],
+                                   lse=part_lse[j], workspace=wss[j], kv_begin=kbs[j], kv_end=kes[j])
+               for j in range(S)]
 
-    def call(_):
-        for f in fns:
-            f()
-        mla.merge_lse(part_out.reshape(S, N, 512), part_lse.reshape(S, N), out=out, lse=lse)
-    call(0)
-    torch.cuda.synchronize()
-    rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(10).choice(
-        N, 16, replace=False)])).astype(np.int64)
-    ro, rl = oracle.decode(q_np, cache.kv, True, cache.kv_scale, cache.block_table,
-                           cache.seq_lens, w.softmax_scale, rows=rows)
-    idx = torch.from_numpy(rows).to(dev)
-    check_out(out[idx], ro, name + " out")
-    check_lse(lse[idx], rl, name + " lse")
-    ms = event_times(torch, stream, call, 30)
-    L = [int(x) for x in cache.seq_lens]
-    ab = sum(acc.decode_bytes(L, P, H, "fp8", out_bytes=4, block_size=cache.block_size,
-                              kv_begin=[lo] * B, kv_end=[hi] * B) for lo, hi in bounds)
-    us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
-    res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
-                 "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
-                 "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4),
-                 "launches": S + 1, "note": "8 partition calls + mla_merge_lse"}
-    log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
-    del kv, part_out, fns
+        def call(_):
+            for f in fns:
+                f()
+            mla.merge_lse(part_out.reshape(S, N, 512), part_lse.reshape(S, N), out=out, lse=lse)
+        call(0)
+        torch.cuda.synchronize()
+        rows = np.unique(np.concatenate([[0, N - 1], np.random.default_rng(10).choice(
+            N, 16, replace=False)])).astype(np.int64)
+        ro, rl = oracle.decode(q_np, cache.kv, True, cache.kv_scale, cache.block_table,
+                               cache.seq_lens, w.softmax_scale, rows=rows)
+        idx = torch.from_numpy(rows).to(dev)
+        check_out(out[idx], ro, name + " out")
+        check_lse(lse[idx], rl, name + " lse")
+        ms = event_times(torch, stream, call, 30)
+        L = [int(x) for x in cache.seq_lens]
+        ab = sum(acc.decode_bytes(L, P, H, "fp8", out_bytes=4, block_size=cache.block_size,
+                                  kv_begin=[lo] * B, kv_end=[hi] * B) for lo, hi in bounds)
+        us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
+        res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
+                     "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
+                     "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4),
+                     "launches": S + 1, "note": "8 partition calls + mla_merge_lse"}
+        log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
+        del kv, part_out, fns
 
-    # cache write: the 32,768 new rows of the prefill workload quantised into a
-    # shuffled FP8 paged cache (64-token blocks)
-    name = "cache_write_t32768_fp8_paged"
-    T = 32768
-    log("generating", name)
-    latent_np = mi.normal_bf16_bits(606, 1, (T, 576))
-    blocks = np.random.default_rng(606).permutation(T // 64 + 8).astype(np.int64)
-    slot_np = (blocks[np.arange(T) // 64] * 64 + np.arange(T) % 64).astype(np.int32)
-    scale = float(np.float32(5.0 / 448.0))
-    latent = bf16_tensor(latent_np, dev).reshape(T, 576)
-    slot_t = torch.from_numpy(slot_np).to(dev)
-    kvc = torch.zeros(((T // 64 + 8) * 64, 576), dtype=torch.uint8, device=dev)
-    mla.cache_write(latent, kvc, slot_t, kv_scale=scale)
-    torch.cuda.synchronize()
-    rows = np.random.default_rng(607).choice(T, 64, replace=False)
-    sub = oracle.cache_write(latent_np[rows], np.arange(64, dtype=np.int32),
-                             np.zeros((64, 576), np.uint8), True, scale)
-    if not np.array_equal(kvc[torch.from_numpy(slot_np[rows]).to(dev)].cpu().numpy(), sub):
-        raise AssertionError(name + ": codes differ from the oracle")
-    ms = event_times(torch, stream, lambda i: mla.cache_write(latent, kvc, slot_t,
-                                                              kv_scale=scale), 50)
-    ab = T * (2 * 576 + 576 + 4)
-    us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
-    res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
-                 "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
-                 "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4)}
-    log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
-    del latent, kvc
+    if want("cache_write_t32768_fp8_paged"):
+        # cache write: the 32,768 new rows of the prefill workload quantised into a
+        # shuffled FP8 paged cache (64-token blocks)
+        name = "cache_write_t32768_fp8_paged"
+        T = 32768
+        log("generating", name)
+        latent_np = mi.normal_bf16_bits(606, 1, (T, 576))
+        blocks = np.random.default_rng(606).permutation(T // 64 + 8).astype(np.int64)
+        slot_np = (blocks[np.arange(T) // 64] * 64 + np.arange(T) % 64).astype(np.int32)
+        scale = float(np.float32(5.0 / 448.0))
+        latent = bf16_tensor(latent_np, dev).reshape(T, 576)
+        slot_t = torch.from_numpy(slot_np).to(dev)
+        kvc = torch.zeros(((T // 64 + 8) * 64, 576), dtype=torch.uint8, device=dev)
+        mla.cache_write(latent, kvc, slot_t, kv_scale=scale)
+        torch.cuda.synchronize()
+        rows = np.random.default_rng(607).choice(T, 64, replace=False)
+        sub = oracle.cache_write(latent_np[rows], np.arange(64, dtype=np.int32),
+                                 np.zeros((64, 576), np.uint8), True, scale)
+        if not np.array_equal(kvc[torch.from_numpy(slot_np[rows]).to(dev)].cpu().numpy(), sub):
+            raise AssertionError(name + ": codes differ from the oracle")
+        ms = event_times(torch, stream, lambda i: mla.cache_write(latent, kvc, slot_t,
+                                                                  kv_scale=scale), 50)
+        ab = T * (2 * 576 + 576 + 4)
+        us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
+        res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
+                     "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
+                     "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4)}
+        log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
+        del latent, kvc
 
-    # top-k renormalisation of the target probabilities after a verify step: 128 rows
-    # (32 sequences x 4 positions) over a 163,840-entry vocabulary, k per row in [1, 100];
-    # 7 rotating copies of the 84 MB input so every call reads HBM
-    name = "top_k_renorm_r128_v163840"
-    w = mi.TOP_K_WORKLOADS[name]
-    log("generating", name)
-    p_np, k_np = w.probs(), w.top_k()
-    copies = 7
-    pin = [torch.from_numpy(p_np).to(dev) for _ in range(copies)]
-    pout = [torch.empty_like(pin[0]) for _ in range(copies)]
-    kt = torch.from_numpy(k_np).to(dev)
-    lib = mla.library()
-    need = mla.top_k_renorm_workspace_size(w.rows, w.vocab)
-    tws = torch.empty(need, dtype=torch.uint8, device=dev)
-    import ctypes
-    sptr = ctypes.c_void_p(stream.cuda_stream)
-    targs = [(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(kt.data_ptr()), w.rows, w.vocab,
-              ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(tws.data_ptr()), need, sptr)
-             for a, b in zip(pin, pout)]
+    if want("top_k_renorm_r128_v163840"):
+        # top-k renormalisation of the target probabilities after a verify step: 128 rows
+        # (32 sequences x 4 positions) over a 163,840-entry vocabulary, k per row in [1, 100];
+        # 7 rotating copies of the 84 MB input so every call reads HBM
+        name = "top_k_renorm_r128_v163840"
+        w = mi.TOP_K_WORKLOADS[name]
+        log("generating", name)
+        p_np, k_np = w.probs(), w.top_k()
+        copies = 7
+        pin = [torch.from_numpy(p_np).to(dev) for _ in range(copies)]
+        pout = [torch.empty_like(pin[0]) for _ in range(copies)]
+        kt = torch.from_numpy(k_np).to(dev)
+        lib = mla.library()
+        need = mla.top_k_renorm_workspace_size(w.rows, w.vocab)
+        tws = torch.empty(need, dtype=torch.uint8, device=dev)
+        import ctypes
+        sptr = ctypes.c_void_p(stream.cuda_stream)
+        targs = [(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(kt.data_ptr()), w.rows, w.vocab,
+                  ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(tws.data_ptr()), need, sptr)
+                 for a, b in zip(pin, pout)]
 
-    def tcall(i):
-        st = lib.mla_top_k_renorm_prob(*targs[i % copies])
-        if st != 0:
-            raise RuntimeError("mla_top_k_renorm_prob failed: %d" % st)
-    for i in range(copies):
-        tcall(i)
-    torch.cuda.synchronize()
-    chk = np.array([0, 1, 63, w.rows - 1])
-    want = oracle.top_k_renorm_prob(p_np[chk], k_np[chk])
-    for j in range(copies):
-        got = pout[j][torch.from_numpy(chk).to(dev)].cpu().numpy()
-        if not np.array_equal(got != 0, want != 0):
-            raise AssertionError(name + ": kept sets differ from the oracle")
-        m = want != 0
-        if np.max(np.abs(got[m] - want[m]) / want[m]) > 2e-6:
-            raise AssertionError(name + ": values differ from the oracle")
-    ms = event_times(torch, stream, tcall, 50)
-    ab = w.rows * w.vocab * 8 + w.rows * 4
-    us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
-    res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
-                 "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
-                 "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4), "input_copies": copies,
-                 "launches": 2}
-    log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
+        def tcall(i):
+            st = lib.mla_top_k_renorm_prob(*targs[i % copies])
+            if st != 0:
+                raise RuntimeError("mla_top_k_renorm_prob failed: %d" % st)
+        for i in range(copies):
+            tcall(i)
+        torch.cuda.synchronize()
+        chk = np.array([0, 1, 63, w.rows - 1])
+        want = oracle.top_k_renorm_prob(p_np[chk], k_np[chk])
+        for j in range(copies):
+            got = pout[j][torch.from_numpy(chk).to(dev)].cpu().numpy()
+            if not np.array_equal(got != 0, want != 0):
+                raise AssertionError(name + ": kept sets differ from the oracle")
+            m = want != 0
+            if np.max(np.abs(got[m] - want[m]) / want[m]) > 2e-6:
+                raise AssertionError(name + ": values differ from the oracle")
+        ms = event_times(torch, stream, tcall, 50)
+        ab = w.rows * w.vocab * 8 + w.rows * 4
+        us = [float(np.percentile(ms, p_)) * 1e3 for p_ in (10, 50, 90)]
+        res[name] = {"us_p10_p50_p90": [round(x, 2) for x in us], "algorithmic_bytes": ab,
+                     "gbs_p50": round(ab / (us[1] * 1e-6) / 1e9, 1),
+                     "hbm_frac_p50": round(ab / (us[1] * 1e-6) / 8e12, 4), "input_copies": copies,
+                     "launches": 2}
+        log("%s: p50 %.1f us, %.0f GB/s" % (name, us[1], res[name]["gbs_p50"]))
     return res
 
 
@@ -371,6 +381,8 @@ def main():
     ap.add_argument("--no-decode", action="store_true",
                     help="prefill figures only (for profiling the prefill kernel)")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--secondary", default="",
+                    help="comma-separated secondary workloads to run (default: all)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (the reference kernel "
                          "for scaling HBM byte counters) and exit")
@@ -408,8 +420,13 @@ def main():
                   "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
                   "data": "synthetic", "config": {"workload": PREFILL_WORKLOAD}}
         import oracle
-        run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
-                    stream, result)
+        if not args.no_prefill:
+            run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
+                        stream, result)
+        if args.secondary:
+            result["secondary"] = secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor,
+                                                    cache_to_device, check_out, check_lse, dev,
+                                                    stream, only=set(args.secondary.split(",")))
         print(json.dumps(result), flush=True)
         return
 
@@ -511,7 +528,8 @@ def main():
     if not args.no_secondary:
         result["secondary"] = secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor,
                                                 cache_to_device, check_out, check_lse, dev,
-                                                stream)
+                                                stream, only=set(args.secondary.split(","))
+                                                if args.secondary else None)
     result["clocks"] = gpu_clocks()
 
     if not args.no_cpu_baseline:
