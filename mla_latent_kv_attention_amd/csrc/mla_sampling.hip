@@ -53,16 +53,26 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 __device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ int digit_bins(int pass) { return pass == 2 ? 1024 : 2048; }
 
+// Inclusive prefix sum over the 64 lanes of a wave: a Hillis-Steele scan within each
+// row of 16 lanes through DPP row shifts (register-to-register, no LDS round trip),
+// then the totals of the rows below added from lanes 15, 31 and 47.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+                 r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+}
+
 // Inclusive prefix sum over the work-group in thread order; *total gets the sum.
 // wsum holds NT / 64 words.
 template <int NT>
 __device__ __forceinline__ uint32_t block_incl_scan(uint32_t v, uint32_t* wsum, uint32_t* total) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+  v = wave_incl_scan(v);
   if (lane == 63) wsum[wv] = v;
   __syncthreads();
   uint32_t before = 0, tot = 0;
@@ -83,13 +93,7 @@ __device__ __forceinline__ void block_incl_scan_n(uint32_t (&v)[W], uint32_t* ws
                                                   uint32_t (&total)[W]) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-#pragma unroll
-    for (int q = 0; q < W; ++q) {
-      const uint32_t t = __shfl_up(v[q], o, 64);
-      if (lane >= o) v[q] += t;
-    }
-  }
+  for (int q = 0; q < W; ++q) v[q] = wave_incl_scan(v[q]);
   if (lane == 63)
 #pragma unroll
     for (int q = 0; q < W; ++q) wsum[W * wv + q] = v[q];
