@@ -276,13 +276,21 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
       if (b < p.B) sr = seq_range(p, b);
       const long long mb = sr.n > 0 ? sr.n + c : 0;
       if (w == 0 && b < p.B && sr.n == 0) write_empty(b);
-      long long incl = mb;
+      long long incl, tot;
+      if (!__builtin_amdgcn_ballot_w64(mb >= (1ll << 25))) {
+        // every count below 2^25: the 32-bit register scan cannot overflow
+        const uint32_t i32 = wave_incl_scan((uint32_t)mb);
+        incl = i32;
+        tot = __builtin_amdgcn_readlane(i32, 63);
+      } else {
+        incl = mb;
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const long long t = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += t;
+        for (int o = 1; o < 64; o <<= 1) {
+          const long long t = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += t;
+        }
+        tot = __shfl(incl, 63, 64);
       }
-      const long long tot = __shfl(incl, 63, 64);
       const int We0 = (int)min((long long)W, tot);
       const long S0_ = w < We0 ? first_step(w, tot, We0) : 0;
       if (lane == 0) seg[2] = tot;

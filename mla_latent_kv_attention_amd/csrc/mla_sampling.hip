@@ -53,20 +53,6 @@ __device__ __forceinline__ float key_value(uint32_t k) {
 __device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
 __device__ __forceinline__ int digit_bins(int pass) { return pass == 2 ? 1024 : 2048; }
 
-// Inclusive prefix sum over the 64 lanes of a wave: a Hillis-Steele scan within each
-// row of 16 lanes through DPP row shifts (register-to-register, no LDS round trip),
-// then the totals of the rows below added from lanes 15, 31 and 47.
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
-  const int lane = threadIdx.x & 63;
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, true);  // row_shr:1
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, true);  // row_shr:2
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, true);  // row_shr:4
-  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, true);  // row_shr:8
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
-                 r2 = __builtin_amdgcn_readlane(v, 47);
-  return v + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
-}
-
 // Inclusive prefix sum over the work-group in thread order; *total gets the sum.
 // wsum holds NT / 64 words.
 template <int NT>
