@@ -40,8 +40,13 @@ def log(*a):
 
 
 def source_hash(name: str) -> str:
+    """Hash of a kernel source with its // comments and blank lines removed, so that
+    counters taken on a kernel stay attached to it through comment-only edits."""
+    import re
     p = os.path.join(ROOT, "mla_latent_kv_attention_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    text = open(p, encoding="utf-8").read()
+    code = [re.sub(r"//.*$", "", l).rstrip() for l in text.splitlines()]
+    return hashlib.sha256("\n".join(l for l in code if l).encode()).hexdigest()[:16]
 
 
 def traffic_from_profile(kernel_file: str, workload: str):

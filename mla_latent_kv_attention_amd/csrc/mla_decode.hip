@@ -21,15 +21,15 @@
 //
 // Per work-group, four waves stream interleaved 16-token steps of a segment.
 // Each wave keeps its own online-softmax state and a 16-row x 512 fp32
-// accumulator, so no wave waits for another until the segment is done (the 16
-// query rows sit in LDS, read by all four).  Per step:
+// accumulator, so no wave waits for another until the segment is done; each
+// wave holds the row block's 18 Q^T fragments in registers.  Per step:
 //   1. every lane loads 8 (bf16) or 16 (fp8) key values of one token straight
 //      from the paged cache into MFMA A-operand registers (16 B per load; fp8
 //      is widened to bf16 exactly); a ring of register buffers keeps the next
-//      2 (fp8) or 1 (bf16) steps in flight, and block ids come through the
-//      scalar cache one step early;
+//      steps in flight (three for fp8 caches, two for bf16), and block ids come
+//      through the scalar cache one step early;
 //   2. S^T[16 tokens x 16 rows] = K Q^T with 18 bf16 MFMA 16x16x32 (Q^T, the
-//      B operand, is read from LDS three k-steps ahead of its MFMA);
+//      B operand, from registers);
 //   3. masking and the softmax numerator run on the 4 scores each lane holds,
 //      with cross-lane max / sum over the 4 lane groups of a row through the
 //      VALU lane swaps (v_permlane16/32_swap, no LDS round trip); each row's
@@ -39,6 +39,8 @@
 //      LDS tile, is read back transposed with ds_read_b64_tr_b16 and feeds
 //      O^T[512 x 16] += V^T P^T with 32 bf16 MFMA 16x16x16; P stays in
 //      registers because the score tile's layout is the B operand's layout.
+//      The two halves are software-pipelined: step i + 1's score half runs
+//      before step i's value half (two value tiles per wave).
 // At the end of a segment the four waves merge through LDS and the work-group
 // writes either the final rows (the piece holds the whole sequence) or its share.
 #include "mla_device.h"
