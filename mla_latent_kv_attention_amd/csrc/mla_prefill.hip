@@ -233,7 +233,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
         sv[i] = (t <= tq) ? sc[i] * p.score_scale_log2 : -INFINITY;
         cm = fmaxf(cm, sv[i]);
       }
-      cm = fmaxf(cm, __shfl_xor(cm, 32));
+      cm = wave_max_xor32(cm);  // the row's other 16 tokens sit in lane l ^ 32
       m_max = fmaxf(m_max, cm);
       m_ref = (m_ref == -INFINITY) ? cm : m_ref;
       const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
@@ -314,8 +314,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   }
 
   // ---- finalize this lane's row
-  const float l_row = l_run + __shfl_xor(l_run, 32);
-  const float lb_row = lb_run + __shfl_xor(lb_run, 32);
+  const float l_row = wave_sum_xor32(l_run);
+  const float lb_row = wave_sum_xor32(lb_run);
   if (!row_ok) return;
   const float inv = (lb_row > 0.f) ? p.out_scale / lb_row : 0.f;
   const size_t orow = (size_t)seq_start * p.H + r;
