@@ -73,6 +73,8 @@ def library() -> ctypes.CDLL:
         lib.mla_top_k_renorm_prob.argtypes = [P, P, I, I, P, P, Z, P]
         lib.mla_top_k_renorm_workspace_size.restype = Z
         lib.mla_top_k_renorm_workspace_size.argtypes = [I, I]
+        lib.mla_hbm_read_probe.restype = I
+        lib.mla_hbm_read_probe.argtypes = [P, Z, P, I, P]
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_status_string.argtypes = [I]
         lib.mla_version.restype = I
@@ -362,6 +364,20 @@ def top_k_renorm_prob(probs: torch.Tensor, top_k: torch.Tensor, *,
                                    _ptr(workspace), workspace.numel(), _stream(dev))
     _check("mla_top_k_renorm_prob", st)
     return out
+
+
+def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, *, grid: int = 1024) -> None:
+    """Launch the plain-read probe over src's bytes (a measurement helper: timed by the
+    caller, it gives the device's rate for a kernel that only reads those bytes).
+    sink: int32 device tensor of at least grid * 256 elements."""
+    if not src.is_contiguous() or src.device.type != "cuda":
+        raise TypeError("src must be a contiguous device tensor")
+    if sink.dtype != torch.int32 or sink.numel() < grid * 256 or sink.device != src.device:
+        raise TypeError("sink must be an int32 tensor of grid * 256 elements on src's device")
+    nbytes = src.numel() * src.element_size()
+    _check("mla_hbm_read_probe",
+           library().mla_hbm_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink), int(grid),
+                                        _stream(src.device)))
 
 
 def default_softmax_scale(qk_dim: int = 192) -> float:

@@ -9,7 +9,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_prefill.hip", "mla_cache.hip", "mla_sampling.hip"]
+SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_prefill.hip", "mla_cache.hip", "mla_sampling.hip",
+           "mla_probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

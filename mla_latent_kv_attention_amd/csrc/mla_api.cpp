@@ -13,7 +13,7 @@
 namespace {
 
 constexpr int kStepTokens = 16;        // tokens per step of the concatenated step list
-constexpr int kMinStepsPerPiece = 8;   // two steps per wave before a piece pays for its merge
+constexpr int kMinStepsPerPiece = 2;   // a short batch still spreads over many CUs
 constexpr int kMaxPiecesPerSeq = 16;   // mean shares per sequence the in-launch merge takes
 // What a piece pays for each sequence it touches (query load, wave merge, partial
 // publish), in 16-token steps of streaming; measured per cache dtype.
@@ -68,12 +68,13 @@ Plan make_plan(int B, int P, int H, int max_kv_len, int num_splits, int cus) {
   const long by_steps = (steps + kMinStepsPerPiece - 1) / kMinStepsPerPiece;
   if (W > by_steps) W = by_steps;
   // The piece that finishes a sequence last merges every share of it through one
-  // CU, which stays cheap up to kMaxPiecesPerSeq shares per sequence: cap there
-  // while the cap still keeps at least half the work-groups.  Batches of very few
-  // sequences take all the pieces instead, and a separate launch merges every row
-  // in parallel (measured: cheaper than a second launch whenever the cap holds).
+  // CU, which stays cheap up to kMaxPiecesPerSeq shares per sequence.  Beyond that
+  // a separate launch merges every row in parallel.  The piece count is never cut
+  // to keep the merge in the launch: idle CUs cost more than the second launch
+  // (measured: 8 sequences x 17,750 keys, 37 us at 128 pieces, 27 us at 256 with
+  // the separate merge; 4 sequences x 4 positions x 32,768 keys, 83 us at 64
+  // pieces, 67 us at 80).
   const long cap = kMaxPiecesPerSeq * Bn;
-  if (W > cap && 2 * cap >= W) W = cap;
   if (W < 1) W = 1;
   pl.W = (int)W;
   pl.merge_in_kernel = pl.W <= cap;

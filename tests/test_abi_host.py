@@ -170,9 +170,8 @@ def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
                                      (1, 1, 12, 16), (0, 1, 12, 0)])
 def test_planner_pieces_fit_the_chip_and_the_work(lib, B, P, H, L):
     """At most one work-group per CU counting the grid's rounding (a multiple of 8
-    pieces when there are several row blocks), at least eight 16-token steps per piece
-    (as far as the max_kv_len hint tells), as many pieces as both allow, and at most 16
-    per sequence where that cap keeps at least half of them."""
+    pieces when there are several row blocks), at least two 16-token steps per piece
+    (as far as the max_kv_len hint tells), and as many pieces as both allow."""
     RB = -(-(P * H) // 16)
     for cus in [80, 256, 304]:
         W = lib.mla_decode_num_splits(B, P, H, L, 0, cus)
@@ -180,10 +179,7 @@ def test_planner_pieces_fit_the_chip_and_the_work(lib, B, P, H, L):
         by_cus = cus // RB
         if RB > 1 and by_cus >= 8:
             by_cus -= by_cus % 8
-        want = max(1, min(by_cus, -(-steps // 8)))
-        cap = 16 * max(B, 1)
-        if want > cap and 2 * cap >= want:
-            want = cap
+        want = max(1, min(by_cus, -(-steps // 2)))
         assert W == want
         assert (-(-W // 8) * 8 * RB if RB > 1 else W) <= max(cus, 8 * RB)
 
@@ -214,3 +210,19 @@ def test_explicit_split_count_is_honoured(lib):
     assert lib.mla_decode_num_splits(2, 1, 12, 1000, 7, 256) == 7
     assert lib.mla_decode_num_splits(2, 1, 12, 10, 3, 256) == 3
     assert lib.mla_decode_num_splits(2, 5, 16, 10, 3, 256) == -2
+
+
+def test_read_probe_rejects_bad_arguments_before_launch(lib):
+    """The measurement helper: null pointers, a size or address not a multiple of 16
+    and grids outside 1 .. 65536 are refused; an empty read launches nothing."""
+    lib.mla_hbm_read_probe.restype = ctypes.c_int
+    lib.mla_hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                       ctypes.c_int, ctypes.c_void_p]
+    P = ctypes.c_void_p(0x1000)
+    assert lib.mla_hbm_read_probe(None, 16, P, 1, None) == -1
+    assert lib.mla_hbm_read_probe(P, 16, None, 1, None) == -1
+    assert lib.mla_hbm_read_probe(P, 17, P, 1, None) == -1
+    assert lib.mla_hbm_read_probe(ctypes.c_void_p(0x1008), 16, P, 1, None) == -1
+    assert lib.mla_hbm_read_probe(P, 16, P, 0, None) == -1
+    assert lib.mla_hbm_read_probe(P, 16, P, 65537, None) == -1
+    assert lib.mla_hbm_read_probe(P, 0, P, 4, None) == 0

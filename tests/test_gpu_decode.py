@@ -325,3 +325,26 @@ def test_full_decode_b8_h12_l142000_fp8_8parts(mla):
     po, pl = run_oracle(q, cache, np.full(B, lo, np.int32), np.full(B, hi, np.int32), rows=rows)
     check_out(parts_o[3][idx], po, "partition 3 out")
     check_lse(parts_l[3][idx], pl, "partition 3 lse")
+
+    # All partitions in one call, as the bench times them: the S x B (partition,
+    # sequence) ranges are S * B sequences of one batch (query and block-table row
+    # repeated, range from kv_begin / kv_end).  Each range's result matches its own
+    # call's; the merge matches the oracle.
+    S = len(bounds)
+    qb = np.tile(q, (S, 1, 1, 1))
+    bc = mi.PagedCache(kv=cache.kv, kv_dtype=cache.kv_dtype, kv_scale=cache.kv_scale,
+                       block_table=np.tile(cache.block_table, (S, 1)),
+                       seq_lens=np.tile(cache.seq_lens, S), block_size=cache.block_size)
+    kb = np.repeat([lo for lo, _ in bounds], B).astype(np.int32)
+    ke = np.repeat([hi for _, hi in bounds], B).astype(np.int32)
+    span = max(hi - lo for lo, hi in bounds)
+    bo, bl = run_gpu(mla, qb, bc, kv_begin=kb, kv_end=ke, max_kv_len=span)
+    bo = bo.reshape(S, B * H, 512)
+    bl = bl.reshape(S, B * H)
+    for j in range(S):
+        assert (bo[j] - parts_o[j]).abs().max().item() < 2e-3
+        assert (bl[j] - parts_l[j]).abs().max().item() < 2e-5
+    bmo, bml = mla.merge_lse(bo, bl)
+    torch.cuda.synchronize()
+    check_out(bmo[idx], ref_o, "batched merged out")
+    check_lse(bml[idx], ref_l, "batched merged lse")
