@@ -44,6 +44,8 @@ constexpr int kDmaPerWave = 10;                  // 4 waves x 10 x 1 KB cover a 
 constexpr int kSlotBytes = 4 * kDmaPerWave * 1024;
 constexpr int kRing = 3;                         // bf16 tiles in flight / in use
 constexpr float kCap = 64.0f;  // log2 units a score may exceed its row's reference max
+constexpr int kKAhead = 3;     // K fragments read this many score MFMAs ahead
+constexpr int kVAhead = 3;     // V^T operands read this many value MFMAs ahead
 
 static_assert(kTile * kPRowChunks <= 4 * kDmaPerWave * 64, "DMA slots must cover a tile");
 
@@ -96,21 +98,6 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Scheduling pattern for a chain of kMfma MFMAs, each fed by kReads LDS reads:
-// the reads for the first kAhead MFMAs go first, then each MFMA is followed by
-// the reads of the MFMA kAhead places later.
-template <int kMfma, int kReads, int kAhead>
-__device__ __forceinline__ void sched_pipeline() {
-  constexpr int kDsRead = 0x100, kMfmaMask = 0x8;
-  __builtin_amdgcn_sched_group_barrier(kDsRead, kReads * kAhead, 0);
-#pragma unroll
-  for (int i = 0; i < kMfma - kAhead; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kMfmaMask, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kDsRead, kReads, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(kMfmaMask, kAhead, 0);
-}
-
 // FP8 tiles go through registers: 16 codes per 16-byte load, widened exactly to
 // bf16 on the way into the same padded LDS layout.
 struct Fp8Stage {
@@ -148,6 +135,7 @@ struct Fp8Stage {
 
 template <bool kFp8>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) {
+  constexpr int KA = kKAhead, VA = kVAhead;
   // bf16: a ring of 3 DMA slots (120 KB); fp8: two register-staged tiles (73 KB)
   __shared__ __attribute__((aligned(16))) uint16_t lds[kFp8 ? 2 * kTileElems : kRing * kSlotBytes / 2];
   const int tid = threadIdx.x;
@@ -209,21 +197,31 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   // per-lane LDS offsets (elements) inside a tile
   const int a_off = n * kPRow + 8 * g;  // K fragment: token n, dims 16 kk + 8 g
   const int v_tok = 4 * g + ((lane & 15) >> 2);
-  const int v_off = v_tok * kPRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int v_off = v_tok * kPRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // one opaque per-lane offset: the loop adds the tile's slot to it once and every
+  // transposed read takes its constant part in the instruction's offset field
+  asm volatile("" : "+v"(v_off));
 
   // Rows whose token precedes the whole tile are fully masked (their P is 0);
   // they still run the MFMAs: an early exit here would split the accumulator's
   // live range and cost far more than the few skipped diagonal tiles.
   auto compute = [&](const uint16_t* buf, int kt) {
     {
-      // K fragments are read two k-steps ahead of the MFMA that consumes them; the
-      // group barriers pin that interleave (left alone, the scheduler waits on each
-      // read right before its MFMA)
       f32x16 sc = {};
+      // K fragments KA MFMAs ahead in a register ring; the order is pinned by
+      // scheduling barriers (left alone, the scheduler issues each read right before
+      // its MFMA and waits for it, exposing the LDS latency once per MFMA)
+      bf16x8 kb[KA + 1];
 #pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk)
-        sc = mfma_32x32x16(*(const bf16x8*)(buf + a_off + 16 * kk), qf[kk], sc);
-      sched_pipeline<kKSteps, 1, 2>();
+      for (int kk = 0; kk < KA; ++kk) kb[kk] = *(const bf16x8*)(buf + a_off + 16 * kk);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        sc = mfma_32x32x16(kb[kk % (KA + 1)], qf[kk], sc);
+        if (kk + KA < kKSteps)
+          kb[(kk + KA) % (KA + 1)] = *(const bf16x8*)(buf + a_off + 16 * (kk + KA));
+        __builtin_amdgcn_sched_barrier(0);
+      }
       // lane (n, g) holds tokens kt*32 + 8 (i/4) + 4 g + i%4 of row n
       float sv[16];
       float cm = -INFINITY;
@@ -257,18 +255,25 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
           lb_run += (float)pf[j][i];
         }
       }
+      // V^T operands VA MFMAs ahead in a register ring, pinned the same way; MFMA m
+      // covers dims 32 (m / 2) .. + 31 and keys 16 (m % 2) .. + 15
+      auto vread = [&](int m) {
+        const uint16_t* src = buf + v_off + (16 * (m & 1)) * kPRow + 32 * (m >> 1);
+        const i16x4 lo = lds_read_tr16(src);
+        const i16x4 hi = lds_read_tr16(src + 8 * kPRow);
+        const i16x8 v8 = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        return __builtin_bit_cast(bf16x8, v8);
+      };
+      bf16x8 vb[VA + 1];
 #pragma unroll
-      for (int mb = 0; mb < 16; ++mb) {
+      for (int m = 0; m < VA; ++m) vb[m] = vread(m);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const uint16_t* src = buf + v_off + (16 * j) * kPRow + 32 * mb;
-          const i16x4 lo = lds_read_tr16(src);
-          const i16x4 hi = lds_read_tr16(src + 8 * kPRow);
-          const i16x8 v8 = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-          acc[mb] = mfma_32x32x16(__builtin_bit_cast(bf16x8, v8), pf[j], acc[mb]);
-        }
+      for (int m = 0; m < 32; ++m) {
+        acc[m >> 1] = mfma_32x32x16(vb[m % (VA + 1)], pf[m & 1], acc[m >> 1]);
+        if (m + VA < 32) vb[(m + VA) % (VA + 1)] = vread(m + VA);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      sched_pipeline<32, 2, 2>();
     }
   };
 
