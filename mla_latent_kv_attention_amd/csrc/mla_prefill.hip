@@ -298,17 +298,36 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
     // tile kt lives in slot kt % 3; tile kt + 2 is copied in while tile kt computes
     const uint32_t base = lds_addr(lds);
     const uint8_t* seq_kv = p.kv + (size_t)seq_start * kRowBytes;
-    dma_tile(seq_kv, len, 0, base, wave, lane);
-    if (n_tiles > 1) dma_tile(seq_kv, len, kTile, base + kSlotBytes, wave, lane);
+    // Byte offsets of this lane's ten chunks within a tile, fixed for the whole loop: a
+    // tile that lies inside the sequence takes them as they are, its first row folded
+    // into the scalar base; only the sequence's last, partial tile clamps rows.
+    uint32_t dma_off[kDmaPerWave];
+#pragma unroll
+    for (int i = 0; i < kDmaPerWave; ++i) {
+      const int pos = 64 * (wave + 4 * i) + lane;
+      int row = pos / kPRowChunks, pc = pos - row * kPRowChunks;
+      if (row >= kTile) row = kTile - 1;
+      if (pc == kPRowChunks - 1) pc = 0;
+      dma_off[i] = (uint32_t)(row * kRowBytes + 16 * pc);
+    }
+    auto copy_tile = [&](int tok0, uint32_t slot) {
+      if (tok0 + kTile <= len) {
+        const uint8_t* tile_kv = seq_kv + (size_t)tok0 * kRowBytes;
+#pragma unroll
+        for (int i = 0; i < kDmaPerWave; ++i) dma16(tile_kv, dma_off[i], slot + 1024 * (wave + 4 * i));
+      } else {
+        dma_tile(seq_kv, len, tok0, slot, wave, lane);
+      }
+    };
+    copy_tile(0, base);
+    if (n_tiles > 1) copy_tile(kTile, base + kSlotBytes);
     for (int kt = 0; kt < n_tiles; ++kt) {
       if (kt + 1 < n_tiles)
         wait_vmcnt<kDmaPerWave>();  // this wave's copies of tile kt have landed
       else
         wait_vmcnt<0>();
       __syncthreads();  // everyone's copies of tile kt landed; tile kt - 1 is no longer read
-      if (kt + 2 < n_tiles)
-        dma_tile(seq_kv, len, (kt + 2) * kTile, base + ((kt + 2) % kRing) * kSlotBytes, wave,
-                 lane);
+      if (kt + 2 < n_tiles) copy_tile((kt + 2) * kTile, base + ((kt + 2) % kRing) * kSlotBytes);
       compute(lds + (kt % kRing) * (kSlotBytes / 2), kt);
     }
   }
