@@ -161,6 +161,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   const int rows = len * p.H;
   const int row0 = blk * kRowsPerWg;
   const int wg_last_tok = min(len - 1, (row0 + kRowsPerWg - 1) / p.H);
+  const int wg_first_tok = row0 / p.H;
   const int n_tiles = wg_last_tok / kTile + 1;
 
   // ---- this lane's query row and its Q^T fragments (B operand, 8 dims per k-step)
@@ -183,14 +184,15 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   // Online softmax with a reference max that never moves inside the key loop: a
   // row's reference is its maximum over the first tile (key 0, visible to every
   // row, is in it); later scores enter as 2^(s - m_ref), exact in bf16 and fp32 up
-  // to 2^kCap, where the exponent is capped while m_max tracks the true maximum.
+  // to 2^kCap, where the exponent is capped while x_max tracks the true maximum.
   // If any row of the work-group went more than kCap above its reference, the
   // whole work-group runs the key loop again, those rows from their true maxima and
   // the others from unchanged references (bit-identical results).  With no
   // data-dependent rescale the accumulator stays in its registers for the loop.
   f32x16 acc[16];
   float m_ref = -INFINITY;
-  float m_max = -INFINITY;
+  float x_max = -INFINITY;  // this lane's largest score relative to the reference
+  bool first_pass = true;
   float l_run = 0.f;   // sum of the fp32 probabilities: the lse
   float lb_run = 0.f;  // sum of their bf16 roundings: the output's normaliser
 
@@ -222,37 +224,53 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
           kb[(kk + KA) % (KA + 1)] = *(const bf16x8*)(buf + a_off + 16 * (kk + KA));
         __builtin_amdgcn_sched_barrier(0);
       }
-      // lane (n, g) holds tokens kt*32 + 8 (i/4) + 4 g + i%4 of row n
-      float sv[16];
-      float cm = -INFINITY;
+      // lane (n, g) holds tokens kt*32 + 8 (i/4) + 4 g + i%4 of row n.  Scores are
+      // taken relative to the row's reference: x = s * scale - m_ref in one fma.  In the
+      // first tile the reference is not set yet: that tile's row maximum becomes it.
+      const int lim = tq - kt * kTile - 4 * g;
+      const bool whole = kt * kTile + kTile - 1 <= wg_first_tok;  // every key visible to every row
+      if (kt == 0 && first_pass) {  // uniform: every lane's reference is unset here
+        float cm = -INFINITY;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int t = kt * kTile + 8 * (i >> 2) + 4 * g + (i & 3);
-        sv[i] = (t <= tq) ? sc[i] * p.score_scale_log2 : -INFINITY;
-        cm = fmaxf(cm, sv[i]);
+        for (int i = 0; i < 16; ++i)
+          cm = fmaxf(cm, (8 * (i >> 2) + (i & 3) <= lim) ? sc[i] * p.score_scale_log2
+                                                         : -INFINITY);
+        m_ref = wave_max_xor32(cm);  // the row's other 16 tokens sit in lane l ^ 32
       }
-      cm = wave_max_xor32(cm);  // the row's other 16 tokens sit in lane l ^ 32
-      m_max = fmaxf(m_max, cm);
-      m_ref = (m_ref == -INFINITY) ? cm : m_ref;
       const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
+      float xv[16];
+      if (whole) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) xv[i] = __builtin_fmaf(sc[i], p.score_scale_log2, -mref);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          xv[i] = (8 * (i >> 2) + (i & 3) <= lim)
+                      ? __builtin_fmaf(sc[i], p.score_scale_log2, -mref) : -INFINITY;
+      }
       float pv[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        pv[i] = fast_exp2(fminf(sv[i] - mref, kCap));
+        x_max = fmaxf(x_max, xv[i]);
+        pv[i] = fast_exp2(fminf(xv[i], kCap));
         l_run += pv[i];
       }
       // k-slot 8 g + s of k-step j holds token 16 j + 8 (s / 4) + 4 g + s % 4: exactly
       // the score values i = 8 j + s this lane already has
       // the value MFMA weighs the keys with P rounded to bf16, and the output is
       // normalised by the sum of those same weights (an exact convex combination of
-      // the values: a key that dominates its row contributes its value unchanged)
+      // the values: a key that dominates its row contributes its value unchanged),
+      // summed pairwise by a bf16 dot product with (1, 1)
       bf16x8 pf[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          pf[j][i] = (__bf16)pv[8 * j + i];
-          lb_run += (float)pf[j][i];
+        for (int i = 0; i < 8; i += 2) {
+          const bf16x2 pair = {(__bf16)pv[8 * j + i], (__bf16)pv[8 * j + i + 1]};
+          pf[j][i] = pair.x;
+          pf[j][i + 1] = pair.y;
+          lb_run = __builtin_amdgcn_fdot2_f32_bf16(pair, (bf16x2){(__bf16)1.0f, (__bf16)1.0f},
+                                                   lb_run, false);
         }
       }
       // V^T operands VA MFMAs ahead in a register ring, pinned the same way; MFMA m
@@ -332,9 +350,13 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
     }
   }
   // a row beyond its cap anywhere in the work-group: all waves run the loop again
-  if (!__syncthreads_or(m_max > m_ref + kCap)) break;
-  // only the rows that went past their cap move; the others recompute bit-identically
-  m_ref = (m_max > m_ref + kCap) ? m_max : m_ref;
+  x_max = wave_max_xor32(x_max);  // the row's (its tokens sit in lanes l and l ^ 32)
+  if (!__syncthreads_or(x_max > kCap)) break;
+  // only the rows that went past their cap move, to their true maximum; the others
+  // recompute bit-identically
+  m_ref = (x_max > kCap) ? m_ref + x_max : m_ref;
+  x_max = -INFINITY;
+  first_pass = false;
   }
 
   // ---- finalize this lane's row
