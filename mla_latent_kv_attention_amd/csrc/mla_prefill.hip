@@ -207,36 +207,45 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   // Rows whose token precedes the whole tile are fully masked (their P is 0);
   // they still run the MFMAs: an early exit here would split the accumulator's
   // live range and cost far more than the few skipped diagonal tiles.
+  // S^T of one tile: K fragments KA MFMAs ahead in a register ring; the order is pinned
+  // by scheduling barriers (left alone, the scheduler issues each read right before
+  // its MFMA and waits for it, exposing the LDS latency once per MFMA)
+  auto scores = [&](const uint16_t* buf) {
+    f32x16 sc = {};
+    bf16x8 kb[KA + 1];
+#pragma unroll
+    for (int kk = 0; kk < KA; ++kk) kb[kk] = *(const bf16x8*)(buf + a_off + 16 * kk);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int kk = 0; kk < kKSteps; ++kk) {
+      sc = mfma_32x32x16(kb[kk % (KA + 1)], qf[kk], sc);
+      if (kk + KA < kKSteps)
+        kb[(kk + KA) % (KA + 1)] = *(const bf16x8*)(buf + a_off + 16 * (kk + KA));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return sc;
+  };
+  // Each row's reference: its maximum over tile 0 (key 0 is visible to every row), set
+  // once before the key loop from a score chain of its own, so the loop carries no
+  // first-tile code.  The row's other 16 tokens sit in lane l ^ 32.
+  auto set_reference = [&](const uint16_t* buf) {
+    const f32x16 sc = scores(buf);
+    const int lim = tq - 4 * g;
+    float cm = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      cm = fmaxf(cm, (8 * (i >> 2) + (i & 3) <= lim) ? sc[i] * p.score_scale_log2 : -INFINITY);
+    m_ref = wave_max_xor32(cm);
+  };
+
   auto compute = [&](const uint16_t* buf, int kt) {
     {
-      f32x16 sc = {};
-      // K fragments KA MFMAs ahead in a register ring; the order is pinned by
-      // scheduling barriers (left alone, the scheduler issues each read right before
-      // its MFMA and waits for it, exposing the LDS latency once per MFMA)
-      bf16x8 kb[KA + 1];
-#pragma unroll
-      for (int kk = 0; kk < KA; ++kk) kb[kk] = *(const bf16x8*)(buf + a_off + 16 * kk);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int kk = 0; kk < kKSteps; ++kk) {
-        sc = mfma_32x32x16(kb[kk % (KA + 1)], qf[kk], sc);
-        if (kk + KA < kKSteps)
-          kb[(kk + KA) % (KA + 1)] = *(const bf16x8*)(buf + a_off + 16 * (kk + KA));
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      const f32x16 sc = scores(buf);
       // lane (n, g) holds tokens kt*32 + 8 (i/4) + 4 g + i%4 of row n.  Scores are
       // taken relative to the row's reference: x = s * scale - m_ref in one fma.  In the
       // first tile the reference is not set yet: that tile's row maximum becomes it.
       const int lim = tq - kt * kTile - 4 * g;
       const bool whole = kt * kTile + kTile - 1 <= wg_first_tok;  // every key visible to every row
-      if (kt == 0 && first_pass) {  // uniform: every lane's reference is unset here
-        float cm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          cm = fmaxf(cm, (8 * (i >> 2) + (i & 3) <= lim) ? sc[i] * p.score_scale_log2
-                                                         : -INFINITY);
-        m_ref = wave_max_xor32(cm);  // the row's other 16 tokens sit in lane l ^ 32
-      }
       const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
       float xv[16];
       if (whole) {
@@ -252,7 +261,9 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         x_max = fmaxf(x_max, xv[i]);
-        pv[i] = fast_exp2(fminf(xv[i], kCap));
+        // no clamp: a pass in which some x exceeds kCap (where 2^x could overflow) is
+        // discarded and run again from zeroed sums, so only x <= kCap reach the output
+        pv[i] = fast_exp2(xv[i]);
         l_run += pv[i];
       }
       // k-slot 8 g + s of k-step j holds token 16 j + 8 (s / 4) + 4 g + s % 4: exactly
@@ -305,6 +316,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
     st.load(p.kv, seq_start, len, 0, tid);
     st.store(lds, tid);
     __syncthreads();
+    if (first_pass) set_reference(lds);
     for (int kt = 0; kt < n_tiles; ++kt) {
       const bool more = kt + 1 < n_tiles;
       if (more) st.load(p.kv, seq_start, len, (kt + 1) * kTile, tid);
@@ -339,6 +351,14 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
     };
     copy_tile(0, base);
     if (n_tiles > 1) copy_tile(kTile, base + kSlotBytes);
+    if (first_pass) {
+      if (n_tiles > 1)
+        wait_vmcnt<kDmaPerWave>();  // this wave's copies of tile 0 have landed
+      else
+        wait_vmcnt<0>();
+      __syncthreads();
+      set_reference(lds);
+    }
     for (int kt = 0; kt < n_tiles; ++kt) {
       if (kt + 1 < n_tiles)
         wait_vmcnt<kDmaPerWave>();  // this wave's copies of tile kt have landed
