@@ -746,36 +746,50 @@ __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p)
 }
 
 // One work-group of 128 threads per row; each thread owns 4 of the 512 dims.  The
-// partial rows are loaded unconditionally (a split without keys for the row left
-// its slot unwritten; its weight selects the value away), so the loads of several
-// splits are in flight together.
+// partials are taken eight at a time, each batch's lse values loaded together with its
+// rows and combined online against a running maximum, so up to eight partials cost one
+// round trip to memory.  A partial that saw no key of the row has lse = -inf and an
+// unwritten row, which its zero weight selects away.
 __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ part_out,
                                                     const float* __restrict__ part_lse, int S,
                                                     int N, void* out, int out_bf16, float* lse) {
+  constexpr int kBatch = 8;
   const int n = blockIdx.x;
   const int d = 4 * threadIdx.x;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[(size_t)s * N + n]);
+  float mx = -INFINITY, L = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  if (M != -INFINITY) {
-#pragma unroll 8
-    for (int s = 0; s < S; ++s) {
-      const float x = part_lse[(size_t)s * N + n];
-      const float w = (x == -INFINITY) ? 0.f : expf(x - M);
-      const f32x4 v = *(const f32x4*)(part_out + ((size_t)s * N + n) * kDV + d);
-      L += w;
-      if (w > 0.f) acc += w * v;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float lv[kBatch];
+    f32x4 v[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const int s = min(s0 + u, S - 1);  // past the end: re-read the last, weight 0
+      lv[u] = (s0 + u < S) ? part_lse[(size_t)s * N + n] : -INFINITY;
+      v[u] = *(const f32x4*)(part_out + ((size_t)s * N + n) * kDV + d);
     }
-    acc *= 1.f / L;
+    float m_new = mx;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) m_new = fmaxf(m_new, lv[u]);
+    if (m_new == -INFINITY) continue;  // nothing seen yet
+    const float r = (mx == -INFINITY) ? 0.f : expf(mx - m_new);
+    L *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const float w = (lv[u] == -INFINITY) ? 0.f : expf(lv[u] - m_new);
+      L += w;
+      if (w > 0.f) acc += w * v[u];
+    }
+    mx = m_new;
   }
+  if (mx != -INFINITY) acc *= 1.f / L;
   if (out_bf16) {
     const bf16x4 o = {(__bf16)acc.x, (__bf16)acc.y, (__bf16)acc.z, (__bf16)acc.w};
     *(bf16x4*)((uint16_t*)out + (size_t)n * kDV + d) = o;
   } else {
     *(f32x4*)((float*)out + (size_t)n * kDV + d) = acc;
   }
-  if (lse && threadIdx.x == 0) lse[n] = (M == -INFINITY) ? -INFINITY : M + logf(L);
+  if (lse && threadIdx.x == 0) lse[n] = (mx == -INFINITY) ? -INFINITY : mx + logf(L);
 }
 
 }  // namespace

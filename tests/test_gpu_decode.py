@@ -140,9 +140,12 @@ def test_late_score_jump(mla, kv_dtype, gain):
     assert ref_l[1, 0, 5] > ref_l[1, 0, 4] + 15  # the planted key dominates that row
 
 
-def test_merge_lse_matches_oracle(mla):
-    rng = np.random.default_rng(7)
-    S, N = 5, 37
+@pytest.mark.parametrize("S", [5, 8, 13, 20])
+def test_merge_lse_matches_oracle(mla, S):
+    """Partials are combined in batches of eight: one batch, exactly one, and several
+    with a ragged last batch."""
+    rng = np.random.default_rng(7 + S)
+    N = 37
     po = rng.standard_normal((S, N, 512)).astype(np.float32)
     pl = (rng.standard_normal((S, N)) * 3).astype(np.float32)
     pl[:, 3] = -np.inf                 # a row with no keys anywhere
