@@ -15,7 +15,8 @@
 // widened exactly on the way in) with the next tile's loads in flight, and
 // read by all four waves:
 //   S^T[32 tokens x 32 rows] = K Q^T           36 MFMA 32x32x16 (A from LDS)
-//   causal mask, online softmax against a per-row reference fixed in the first tile
+//   causal mask, online softmax against a per-row reference fixed from the first
+//   tile before the key loop
 //   O^T[512 x 32 rows] += V^T P^T               32 MFMA 32x32x16 (A = V^T read
 //                                               with ds_read_b64_tr_b16, B = P^T
 //                                               straight from the score registers)
@@ -185,12 +186,13 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
 
   // Online softmax with a reference max that never moves inside the key loop: a
   // row's reference is its maximum over the first tile (key 0, visible to every
-  // row, is in it); later scores enter as 2^(s - m_ref), exact in bf16 and fp32 up
-  // to 2^kCap, where the exponent is capped while x_max tracks the true maximum.
-  // If any row of the work-group went more than kCap above its reference, the
-  // whole work-group runs the key loop again, those rows from their true maxima and
-  // the others from unchanged references (bit-identical results).  With no
-  // data-dependent rescale the accumulator stays in its registers for the loop.
+  // row, is in it); every score enters as 2^(s - m_ref), exact in bf16 and fp32 up
+  // to 2^kCap, while x_max tracks the largest s - m_ref.  If any row of the
+  // work-group went more than kCap above its reference, that pass is discarded and
+  // the whole work-group runs the key loop again from zeroed sums, those rows from
+  // their true maxima and the others from unchanged references (bit-identical
+  // results).  With no data-dependent rescale the accumulator stays in its registers
+  // for the loop.
   f32x16 acc[16];
   float m_ref = -INFINITY;
   float x_max = -INFINITY;  // this lane's largest score relative to the reference
@@ -244,8 +246,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
     {
       const f32x16 sc = scores(buf);
       // lane (n, g) holds tokens kt*32 + 8 (i/4) + 4 g + i%4 of row n.  Scores are
-      // taken relative to the row's reference: x = s * scale - m_ref in one fma.  In the
-      // first tile the reference is not set yet: that tile's row maximum becomes it.
+      // taken relative to the row's reference: x = s * scale - m_ref in one fma.
       const int lim = tq - kt * kTile - 4 * g;
       const bool whole = kt * kTile + kTile - 1 <= wg_first_tok;  // every key visible to every row
       const float mref = (m_ref == -INFINITY) ? 0.f : m_ref;
