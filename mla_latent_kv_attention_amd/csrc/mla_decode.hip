@@ -663,55 +663,66 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
   }
 }
 
-// The merge of sequences split into many shares, as a launch of its own: one
-// 256-thread work-group per output row.  8 groups of 32 threads take every 8th
-// share (each thread 16 of the 512 dims), four shares' loads in flight at a time,
-// each group combining its shares online against a running maximum; the groups'
-// results meet in LDS.  The decode launch that wrote the shares has completed, so
-// plain loads see them.  A share that saw no key of the row has lse = -inf and an
-// unwritten row, which its zero weight selects away.
+// The merge of sequences split into many shares, as a launch of its own: kQ
+// 256-thread work-groups per output row, each owning 512 / kQ of its dims.  8 groups of
+// 32 threads take every 8th share, each thread 16 / kQ dims, the loads of 4 kQ shares
+// in flight per group (the same registers whatever kQ), combined online against a
+// running maximum; the groups' results meet in LDS.  kQ = 4 takes a row's shares in a
+// quarter of the rounds, for sequences spread over many pieces (one long sequence);
+// kQ = 1 launches a quarter of the work-groups, for many rows with few shares each.
+// The decode launch that wrote the shares has completed, so plain loads see them.  A
+// share that saw no key of the row has lse = -inf and an unwritten row, which its
+// zero weight selects away.
+template <int kQ>
 __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p) {
-  __shared__ float red[8][kDV + 4];
+  constexpr int kDims = kDV / kQ;        // dims of the row this work-group owns
+  constexpr int kVec = 4 / kQ;           // f32x4 per thread and share
+  constexpr int kBatch = 4 * kQ;         // shares in flight per group
+  __shared__ float red[8][kDims + 4];
   __shared__ float gm[8], gl[8];
   const int tid = threadIdx.x;
-  const size_t n = blockIdx.x;
+  const size_t n = blockIdx.x / kQ;
+  const int d0 = (int)(blockIdx.x % kQ) * kDims;
   const int b = (int)(n / p.R), rr = (int)(n % p.R);
   const int w_first = p.seq_pieces[2 * b], w_last = p.seq_pieces[2 * b + 1];
   if (w_first == w_last) return;  // one piece held the whole sequence and wrote it
   const size_t R = p.R;
   const float* lse_b = p.part_lse + (size_t)b * R + rr;  // share v at v * R
   const int g = tid >> 5, l = tid & 31;
-  f32x4 o4[4] = {};
+  f32x4 o4[kVec] = {};
   float mx = -INFINITY, ls = 0.f;
-  for (int v0 = w_first + g; v0 <= w_last; v0 += 32) {
-    float l4[4];
-    f32x4 t[4][4];
+  for (int v0 = w_first + g; v0 <= w_last; v0 += 8 * kBatch) {
+    float l4[kBatch];
+    f32x4 t[kBatch][kVec];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       const int v = min(v0 + 8 * u, w_last);  // past the end: re-read, weight 0
       l4[u] = (v0 + 8 * u <= w_last) ? lse_b[v * R] : -INFINITY;
-      const f32x4* src = (const f32x4*)(p.part_out + ((size_t)(v + b) * R + rr) * kDV + 16 * l);
+      const f32x4* src =
+          (const f32x4*)(p.part_out + ((size_t)(v + b) * R + rr) * kDV + d0 + 4 * kVec * l);
 #pragma unroll
-      for (int k = 0; k < 4; ++k) t[u][k] = src[k];
+      for (int k = 0; k < kVec; ++k) t[u][k] = src[k];
     }
-    const float m_new = fmaxf(fmaxf(mx, fmaxf(l4[0], l4[1])), fmaxf(l4[2], l4[3]));
+    float m_new = mx;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) m_new = fmaxf(m_new, l4[u]);
     if (m_new == -INFINITY) continue;
     const float r = (mx == -INFINITY) ? 0.f : expf(mx - m_new);
     ls *= r;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o4[k] *= r;
+    for (int k = 0; k < kVec; ++k) o4[k] *= r;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       const float wt = (l4[u] == -INFINITY) ? 0.f : expf(l4[u] - m_new);
       ls += wt;
       if (wt > 0.f)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o4[k] += wt * t[u][k];
+        for (int k = 0; k < kVec; ++k) o4[k] += wt * t[u][k];
     }
     mx = m_new;
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) *(f32x4*)&red[g][16 * l + 4 * k] = o4[k];
+  for (int k = 0; k < kVec; ++k) *(f32x4*)&red[g][4 * kVec * l + 4 * k] = o4[k];
   if (l == 0) {
     gm[g] = mx;
     gl[g] = ls;
@@ -726,23 +737,35 @@ __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p)
     sc[i] = (gm[i] == -INFINITY) ? 0.f : expf(gm[i] - M);
     wsum += gl[i] * sc[i];
   }
-  // thread tid writes dims 2 tid, 2 tid + 1
-  float2 v2 = {0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    v2.x += red[i][2 * tid] * sc[i];
-    v2.y += red[i][2 * tid + 1] * sc[i];
-  }
   const float il = (M != -INFINITY && wsum > 0.f) ? 1.f / wsum : 0.f;
-  v2.x *= il;
-  v2.y *= il;
-  if (p.out_bf16) {
-    const bf16x2 ob = {(__bf16)v2.x, (__bf16)v2.y};
-    *(bf16x2*)((uint16_t*)p.out + n * kDV + 2 * tid) = ob;
-  } else {
-    *(float2*)((float*)p.out + n * kDV + 2 * tid) = v2;
+  // thread tid writes dims d0 + kDims / 256 * tid ..
+  constexpr int kPer = kDims / 256;  // 2 (kQ = 1) or 0 (kQ = 4: half the threads write one)
+  if constexpr (kPer == 2) {
+    float2 v2 = {0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      v2.x += red[i][2 * tid] * sc[i];
+      v2.y += red[i][2 * tid + 1] * sc[i];
+    }
+    v2.x *= il;
+    v2.y *= il;
+    if (p.out_bf16) {
+      const bf16x2 ob = {(__bf16)v2.x, (__bf16)v2.y};
+      *(bf16x2*)((uint16_t*)p.out + n * kDV + d0 + 2 * tid) = ob;
+    } else {
+      *(float2*)((float*)p.out + n * kDV + d0 + 2 * tid) = v2;
+    }
+  } else if (tid < kDims) {
+    float x = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x += red[i][tid] * sc[i];
+    x *= il;
+    if (p.out_bf16)
+      ((__bf16*)p.out)[n * kDV + d0 + tid] = (__bf16)x;
+    else
+      ((float*)p.out)[n * kDV + d0 + tid] = x;
   }
-  if (p.lse && tid == 0) p.lse[n] = (M == -INFINITY) ? -INFINITY : M + logf(wsum);
+  if (p.lse && d0 == 0 && tid == 0) p.lse[n] = (M == -INFINITY) ? -INFINITY : M + logf(wsum);
 }
 
 // One work-group of 128 threads per row; each thread owns 4 of the 512 dims.  The
@@ -809,8 +832,15 @@ hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream)
 hipError_t launch_merge_shares(const DecodeParams& p, hipStream_t stream) {
   const long rows = (long)p.B * p.R;
   if (rows == 0) return hipSuccess;
-  if (rows > 0x7fffffffL) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_shares_kernel, dim3((unsigned)rows), dim3(256), 0, stream, p);
+  // one round of loads per row covers 32 shares with whole-row work-groups: split the
+  // rows into quarters when the sequences average more shares than that
+  const bool quarters = p.W > 32L * p.B;
+  const long groups = rows * (quarters ? 4 : 1);
+  if (groups > 0x7fffffffL) return hipErrorInvalidValue;
+  if (quarters)
+    hipLaunchKernelGGL(merge_shares_kernel<4>, dim3((unsigned)groups), dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL(merge_shares_kernel<1>, dim3((unsigned)groups), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -85,9 +85,12 @@ def test_block_sizes(mla, block_size):
     check_lse(lse, ref_l)
 
 
-def test_bf16_output(mla):
+@pytest.mark.parametrize("num_splits", [0, 200])
+def test_bf16_output(mla, num_splits):
+    """Automatic plan (the separate merge over whole rows) and 200 pieces for 3
+    sequences (the separate merge over row quarters)."""
     q, cache = small_case(2003, [3, 90, 1500], 16, 4, "bf16")
-    out, lse = run_gpu(mla, q, cache, out_dtype=torch.bfloat16)
+    out, lse = run_gpu(mla, q, cache, out_dtype=torch.bfloat16, num_splits=num_splits)
     assert out.dtype == torch.bfloat16
     ref_o, ref_l = run_oracle(q, cache)
     check_out(out, ref_o)
