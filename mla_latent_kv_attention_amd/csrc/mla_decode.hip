@@ -124,18 +124,6 @@ __device__ __forceinline__ int owner(long s, long N, int W) {
   return (int)div_nonneg((s + 1) * W - 1, N);
 }
 
-// Max / sum over the 16 lanes of a row group (lanes 16 g .. 16 g + 15).
-__device__ __forceinline__ float max16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-__device__ __forceinline__ float sum16(float v) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // Last piece of sequence b: combine the partials of pieces w_first..w_last for
 // row rr (16 threads per row, 4 dims each per 64-dim slab).  The pieces are taken
 // four at a time, each batch's lse values loaded together with its partial rows,
