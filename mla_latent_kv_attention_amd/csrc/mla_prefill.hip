@@ -41,14 +41,16 @@ constexpr int kRowBytes = 2 * kDK;               // 1152: one bf16 latent row
 constexpr int kPRowChunks = kRowBytes / 16 + 1;  // 73 16-byte chunks: 72 of data + 1 pad
 constexpr int kPRow = 8 * kPRowChunks;           // padded LDS row (bf16 elements)
 constexpr int kTileElems = kTile * kPRow;
-constexpr int kDmaPerWave = 10;                  // 4 waves x 10 x 1 KB cover a padded tile
-constexpr int kSlotBytes = 4 * kDmaPerWave * 1024;
-constexpr int kRing = 3;                         // bf16 tiles in flight / in use
+constexpr int kDmaPerWave = 10;                  // copies per wave and tile (the last repeats)
+constexpr int kDmaBlocks = 37;                   // 1 KB blocks that cover a padded tile
+constexpr int kSlotBytes = kDmaBlocks * 1024;
+constexpr int kRing = 4;                         // bf16 tiles: two in use, two in flight
 constexpr float kCap = 64.0f;  // log2 units a score may exceed its row's reference max
 constexpr int kKAhead = 3;     // K fragments read this many score MFMAs ahead
 constexpr int kVAhead = 3;     // V^T operands read this many value MFMAs ahead
 
-static_assert(kTile * kPRowChunks <= 4 * kDmaPerWave * 64, "DMA slots must cover a tile");
+static_assert(kTile * kPRowChunks <= kDmaBlocks * 64, "DMA slots must cover a tile");
+static_assert(4 * kDmaPerWave >= kDmaBlocks, "the waves' copies must cover every block");
 
 // One 16-byte global -> LDS copy per lane, no VGPR staging: lane l reads
 // base + voff and lands at LDS byte lds_base + 16 l.  Issued through asm so the
@@ -85,7 +87,8 @@ __device__ __forceinline__ void dma_tile(const uint8_t* seq_kv, int len, int tok
   asm volatile("" : "+v"(l));
 #pragma unroll
   for (int i = 0; i < kDmaPerWave; ++i) {
-    const int inst = wave + 4 * i;
+    // block wave + 4 i; the waves' spare copies repeat the last block (same bytes)
+    const int inst = min(wave + 4 * i, kDmaBlocks - 1);
     const int pos = 64 * inst + l;
     int row = pos / kPRowChunks, pc = pos - row * kPRowChunks;
     if (row >= kTile) row = kTile - 1;
@@ -139,7 +142,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   // fp8 tiles are staged through registers, which leaves room for a shallower ring
   // (measured: 12.6 ms at depth 2 against 14.3 ms at depth 3 on the 32,768-token shape)
   constexpr int KA = kFp8 ? 2 : kKAhead, VA = kFp8 ? 2 : kVAhead;
-  // bf16: a ring of 3 DMA slots (120 KB); fp8: two register-staged tiles (73 KB)
+  // bf16: a ring of 4 DMA slots (148 KB); fp8: two register-staged tiles (73 KB)
   __shared__ __attribute__((aligned(16))) uint16_t lds[kFp8 ? 2 * kTileElems : kRing * kSlotBytes / 2];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -328,7 +331,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
       __syncthreads();
     }
   } else {
-    // tile kt lives in slot kt % 3; tile kt + 2 is copied in while tile kt computes
+    // tile kt lives in slot kt % 4
     const uint32_t base = lds_addr(lds);
     const uint8_t* seq_kv = p.kv + (size_t)seq_start * kRowBytes;
     // Byte offsets of this lane's ten chunks within a tile, fixed for the whole loop: a
@@ -337,7 +340,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
     uint32_t dma_off[kDmaPerWave];
 #pragma unroll
     for (int i = 0; i < kDmaPerWave; ++i) {
-      const int pos = 64 * (wave + 4 * i) + lane;
+      const int pos = 64 * min(wave + 4 * i, kDmaBlocks - 1) + lane;
       int row = pos / kPRowChunks, pc = pos - row * kPRowChunks;
       if (row >= kTile) row = kTile - 1;
       if (pc == kPRowChunks - 1) pc = 0;
@@ -347,7 +350,8 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
       if (tok0 + kTile <= len) {
         const uint8_t* tile_kv = seq_kv + (size_t)tok0 * kRowBytes;
 #pragma unroll
-        for (int i = 0; i < kDmaPerWave; ++i) dma16(tile_kv, dma_off[i], slot + 1024 * (wave + 4 * i));
+        for (int i = 0; i < kDmaPerWave; ++i)
+          dma16(tile_kv, dma_off[i], slot + 1024 * min(wave + 4 * i, kDmaBlocks - 1));
       } else {
         dma_tile(seq_kv, len, tok0, slot, wave, lane);
       }
@@ -362,13 +366,17 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
       __syncthreads();
       set_reference(lds);
     }
+    // Tiles go in pairs: one wait and one work-group barrier per two tiles.  At an even
+    // tile kt the copies in flight are tiles kt and kt + 1 (issued two tiles earlier);
+    // once everyone's have landed, tiles kt - 2 and kt - 1 are no longer read and their
+    // slots take tiles kt + 2 and kt + 3.
     for (int kt = 0; kt < n_tiles; ++kt) {
-      if (kt + 1 < n_tiles)
-        wait_vmcnt<kDmaPerWave>();  // this wave's copies of tile kt have landed
-      else
+      if ((kt & 1) == 0) {
         wait_vmcnt<0>();
-      __syncthreads();  // everyone's copies of tile kt landed; tile kt - 1 is no longer read
-      if (kt + 2 < n_tiles) copy_tile((kt + 2) * kTile, base + ((kt + 2) % kRing) * kSlotBytes);
+        __syncthreads();
+        if (kt + 2 < n_tiles) copy_tile((kt + 2) * kTile, base + ((kt + 2) % kRing) * kSlotBytes);
+        if (kt + 3 < n_tiles) copy_tile((kt + 3) * kTile, base + ((kt + 3) % kRing) * kSlotBytes);
+      }
       compute(lds + (kt % kRing) * (kSlotBytes / 2), kt);
     }
   }
