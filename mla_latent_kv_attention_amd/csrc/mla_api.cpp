@@ -59,11 +59,8 @@ Plan make_plan(int B, int P, int H, int max_kv_len, int num_splits, int cus) {
     pl.merge_in_kernel = pl.W <= kMaxPiecesPerSeq * Bn;
     return pl;
   }
+  // one work-group per CU (the grid is W x RB), so no piece waits for a CU to free up
   long W = (cus > 0 ? cus : 256) / pl.RB;
-  // With several row blocks the grid is W rounded up to 8 per row block (the row
-  // blocks of a piece share an XCD); W itself a multiple of 8 keeps that grid
-  // within one work-group per CU, so no piece waits for a CU to free up.
-  if (pl.RB > 1 && W >= 8) W -= W % 8;
   const long steps = Bn * (((long)max_kv_len + kStepTokens - 1) / kStepTokens);
   const long by_steps = (steps + kMinStepsPerPiece - 1) / kMinStepsPerPiece;
   if (W > by_steps) W = by_steps;

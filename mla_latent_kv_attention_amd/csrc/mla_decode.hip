@@ -218,13 +218,16 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15;  // token (A rows) / query row (B, C columns)
   const int grp = lane >> 4;  // k-group (A, B) / 4-row group (C)
-  // Work-group -> (piece, row block).  The RB row blocks of one piece get ids
-  // congruent mod 8, so they run on one XCD and read the piece's rows through
-  // one L2.
+  // Work-group -> (piece, row block).  In each complete group of 8 pieces the RB
+  // row blocks of a piece get ids congruent mod 8, so they run on one XCD and read
+  // the piece's rows through one L2; the last W % 8 pieces take the remaining ids
+  // with their row blocks side by side, so the grid is exactly W x RB.
   const int W = p.W;
   const int per = 8 * p.RB;
-  const int rb = (blockIdx.x % per) / 8;
-  const int w = (blockIdx.x / per) * 8 + blockIdx.x % 8;
+  const int full = (W / 8) * per;
+  const int id = blockIdx.x;
+  const int rb = id < full ? (id % per) / 8 : (id - full) % p.RB;
+  const int w = id < full ? (id / per) * 8 + id % 8 : 8 * (W / 8) + (id - full) / p.RB;
   if (w >= W) return;
   const size_t row_bytes = kFp8 ? kDK : 2 * kDK;
   uint16_t* vt = sm.v[wave];
@@ -805,7 +808,7 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
 
 }  // namespace
 
-int decode_grid_size(int W, int RB) { return ((W + 7) / 8) * 8 * RB; }
+int decode_grid_size(int W, int RB) { return W * RB; }
 
 hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream) {
   const int grid = decode_grid_size(p.W, p.RB);

@@ -169,19 +169,16 @@ def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
                                      (4, 4, 16, 32768), (8, 1, 12, 17750), (3, 2, 8, 64),
                                      (1, 1, 12, 16), (0, 1, 12, 0)])
 def test_planner_pieces_fit_the_chip_and_the_work(lib, B, P, H, L):
-    """At most one work-group per CU counting the grid's rounding (a multiple of 8
-    pieces when there are several row blocks), at least two 16-token steps per piece
-    (as far as the max_kv_len hint tells), and as many pieces as both allow."""
+    """At most one work-group per CU (the grid is pieces x row blocks), at least two
+    16-token steps per piece (as far as the max_kv_len hint tells), and as many pieces
+    as both allow."""
     RB = -(-(P * H) // 16)
     for cus in [80, 256, 304]:
         W = lib.mla_decode_num_splits(B, P, H, L, 0, cus)
         steps = max(B, 1) * (-(-L // 16))
-        by_cus = cus // RB
-        if RB > 1 and by_cus >= 8:
-            by_cus -= by_cus % 8
-        want = max(1, min(by_cus, -(-steps // 2)))
+        want = max(1, min(cus // RB, -(-steps // 2)))
         assert W == want
-        assert (-(-W // 8) * 8 * RB if RB > 1 else W) <= max(cus, 8 * RB)
+        assert W * RB <= cus
 
 
 @pytest.mark.parametrize("B,P,H,L,S", [(32, 1, 12, 16384, 0), (4, 4, 12, 32768, 0),
