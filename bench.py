@@ -315,6 +315,13 @@ def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device,
             % (name, b2b, b2b_calls, us[1], res[name]["gbs_back_to_back"]))
         del kv, part_out, fns, fb
 
+    if want("prefill_t32768_h12_fp8"):
+        # the same causal prefill over an FP8 latent cache (per-tensor scale): the same
+        # seed and shape as the BF16 workload, its rows quantised to E4M3FN
+        pw = mi.PrefillWorkload("prefill_t32768_h12_fp8", [32768], 12, "fp8", seed=404)
+        res[pw.name] = time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out,
+                                    check_lse, dev, stream, pw, 5)
+
     if want("cache_write_t32768_fp8_paged"):
         # cache write: the 32,768 new rows of the prefill workload quantised into a
         # shuffled FP8 paged cache (64-token blocks)
@@ -398,33 +405,38 @@ def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device,
     return res
 
 
-def run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
-                stream, result):
-    """Causal prefill of the 32K x 12-head workload: parity on sampled tokens, then timing."""
-    pw = mi.WORKLOADS[PREFILL_WORKLOAD]
+def time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev, stream,
+                 pw, steps):
+    """One causal prefill workload: parity on sampled tokens against the oracle, then the
+    mean of `steps` HIP-event-timed calls."""
     log("generating", pw.name)
     pd = mi.prefill_inputs(pw)
     T = pw.total_tokens
+    fp8 = pw.kv_dtype == "fp8"
     pq = bf16_tensor(pd["q"], dev).reshape(T, pw.heads, 576)
-    pkv = bf16_tensor(pd["kv"], dev).reshape(T, 576)
+    if fp8:
+        pkv = torch.from_numpy(np.ascontiguousarray(pd["kv"])).to(dev).reshape(T, 576)
+    else:
+        pkv = bf16_tensor(pd["kv"], dev).reshape(T, 576)
+    kv_scale = float(pd["kv_scale"]) if fp8 else 1.0
     cu = torch.from_numpy(pd["cu_seqlens"]).to(dev)
     pout = torch.empty((T, pw.heads, 512), dtype=torch.bfloat16, device=dev)
     plse = torch.empty((T, pw.heads), dtype=torch.float32, device=dev)
 
     def pstep():
-        mla.prefill(pq, pkv, cu, softmax_scale=pw.softmax_scale, max_seqlen=T,
-                    out_dtype=torch.bfloat16, out=pout, lse=plse)
+        mla.prefill(pq, pkv, cu, softmax_scale=pw.softmax_scale, kv_scale=kv_scale,
+                    max_seqlen=T, out_dtype=torch.bfloat16, out=pout, lse=plse)
     pstep()
     torch.cuda.synchronize()
     toks = np.array([0, 1, 4095, T - 1], np.int64)
-    ro, rl = oracle.prefill(pd["q"], pd["kv"], False, 1.0, pd["cu_seqlens"],
+    ro, rl = oracle.prefill(pd["q"], pd["kv"], fp8, kv_scale, pd["cu_seqlens"],
                             pw.softmax_scale, tokens=toks)
     ti = torch.from_numpy(toks).to(dev)
-    check_out(pout[ti], ro, "prefill out")
-    check_lse(plse[ti], rl, "prefill lse")
+    check_out(pout[ti], ro, pw.name + " out")
+    check_lse(plse[ti], rl, pw.name + " lse")
     pstep()
     pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.prefill_steps)]
+          for _ in range(steps)]
     torch.cuda.synchronize()
     for a, b in pe:
         a.record(stream)
@@ -434,14 +446,22 @@ def run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check
     pms = np.array([a.elapsed_time(b) for a, b in pe])
     pflops = acc.prefill_flops(pw.seq_lens, pw.heads)
     tflops = pflops / (pms.mean() * 1e-3) / 1e12
-    result["prefill"] = {
-        "workload": PREFILL_WORKLOAD, "tokens_per_s": round(T / (pms.mean() * 1e-3), 1),
+    log("%s: %.2f ms, %.0f tok/s, %.1f TFLOP/s" % (pw.name, pms.mean(),
+                                                  T / (pms.mean() * 1e-3), tflops))
+    return {
+        "workload": pw.name, "tokens_per_s": round(T / (pms.mean() * 1e-3), 1),
         "ms": round(float(pms.mean()), 3), "tflops": round(tflops, 1),
         "mfma_frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
         "peak_tflops": BF16_MFMA_PEAK_TFLOPS, "algorithmic_flops": pflops,
-        "kernel": "prefill_kernel<bf16>"}
-    log("prefill: %.2f ms, %.0f tok/s, %.1f TFLOP/s" % (pms.mean(), T / (pms.mean() * 1e-3),
-                                                      tflops))
+        "kernel": "prefill_kernel<%s>" % pw.kv_dtype}
+
+
+def run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
+                stream, result):
+    """Causal prefill of the 32K x 12-head workload: parity on sampled tokens, then timing."""
+    result["prefill"] = time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out,
+                                     check_lse, dev, stream, mi.WORKLOADS[PREFILL_WORKLOAD],
+                                     args.prefill_steps)
 
 
 def main():
