@@ -63,15 +63,23 @@ def traffic_from_profile(kernel_file: str, workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def host_cores() -> int:
+    """CPU cores this process may run on (its affinity mask), the oracle's thread count."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(q, cache, alg_bytes, min_seconds=10.0, max_reps=400):
     """The FP64 oracle on the whole batch (every row), repeated until >= min_seconds."""
     import oracle
     import mla_inputs as mi
-    threads = oracle.max_threads()
+    threads = host_cores()
     reps, t0 = 0, time.perf_counter()
     while True:
         oracle.decode(q, cache.kv, cache.kv_dtype == "fp8", cache.kv_scale, cache.block_table,
-                      cache.seq_lens, mi.softmax_scale_for())
+                      cache.seq_lens, mi.softmax_scale_for(), threads=threads)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or reps >= max_reps:
@@ -79,7 +87,39 @@ def cpu_baseline(q, cache, alg_bytes, min_seconds=10.0, max_reps=400):
     return {"value": alg_bytes * reps / el / 1e9, "unit": "GB/s", "cores": threads,
             "kind": "oracle",
             "sample": "the whole %s batch (all 384 query rows), %d pass(es), %.1f s of FP64 "
-                      "oracle time on %d threads" % (DECODE_WORKLOAD, reps, el, threads)}
+                      "oracle time on %d threads (the process's CPU affinity)"
+                      % (DECODE_WORKLOAD, reps, el, threads)}
+
+
+def prefill_cpu_baseline(pd, pw, min_seconds=10.0, chunk=64, max_chunks=64):
+    """The FP64 oracle on a stratified sample of the prefill's tokens, all heads: chunk c
+    takes the tokens floor((k + (c * 0.618) mod 1) * T / chunk), k = 0 .. chunk - 1, one per
+    equal slice of the sequence.  A token's work grows with its position (token i sees i + 1
+    keys), and each chunk has one token in every slice, so the sample's mean work per token
+    is the whole prefill's to within one slice; tokens/s of the sample is reported as the
+    whole job's rate, with the flop rate of the tokens actually computed beside it."""
+    import oracle
+    T = pw.total_tokens
+    threads = host_cores()
+    fp8 = pw.kv_dtype == "fp8"
+    done, flops, c, t0 = 0, 0, 0, time.perf_counter()
+    while True:
+        off = (c * 0.6180339887) % 1.0
+        toks = np.minimum(((np.arange(chunk) + off) * T / chunk).astype(np.int64), T - 1)
+        oracle.prefill(pd["q"], pd["kv"], fp8, float(pd["kv_scale"]) if fp8 else 1.0,
+                       pd["cu_seqlens"], pw.softmax_scale, tokens=toks, threads=threads)
+        done += len(toks)
+        flops += int(np.sum(toks + 1)) * pw.heads * 2176
+        c += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or c >= max_chunks:
+            break
+    return {"value": round(done / el, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "gflops": round(flops / el / 1e9, 2),
+            "sample": "%d of the %d tokens (all %d heads) of %s, %d stratified chunks of %d (one "
+                      "token per 1/%d of the sequence), %.1f s of FP64 oracle time on %d threads "
+                      "(the process's CPU affinity); rate = sampled tokens / time"
+                      % (done, T, pw.heads, pw.name, c, chunk, chunk, el, threads)}
 
 
 def gpu_clocks():
@@ -158,16 +198,17 @@ def graph_replay_us(torch, fns, out, calls=100, replays=5):
     return a.elapsed_time(b) * 1e3 / (replays * calls)
 
 
-def read_ceiling_gbs(torch, mla, stream, nbytes, copies, calls=30):
+def read_ceiling_gbs(torch, stream, nbytes, copies, calls=30):
     """Rate of a kernel that only reads nbytes (the headline's algorithmic bytes) once,
     over `copies` rotating buffers like the KV pools: back-to-back HIP-event time per
     call, best over a few grid sizes."""
+    from mla_latent_kv_attention_amd.read_probe import hbm_read_probe
     n = (nbytes + 15) // 16 * 16
     bufs = [torch.ones(n, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
     sink = torch.empty(65536 * 256, dtype=torch.int32, device="cuda:0")
     best, grids = None, [512, 1024, 2048]
     for g in grids:
-        us = back_to_back_us(torch, stream, lambda i: mla.hbm_read_probe(
+        us = back_to_back_us(torch, stream, lambda i: hbm_read_probe(
             bufs[i % copies], sink, grid=g), calls)
         best = us if best is None else min(best, us)
     del bufs
@@ -458,10 +499,15 @@ def time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse,
 
 def run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
                 stream, result):
-    """Causal prefill of the 32K x 12-head workload: parity on sampled tokens, then timing."""
-    result["prefill"] = time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out,
-                                     check_lse, dev, stream, mi.WORKLOADS[PREFILL_WORKLOAD],
-                                     args.prefill_steps)
+    """Causal prefill of the 32K x 12-head workload: parity on sampled tokens, timing, and
+    the oracle's rate on a bounded sample of the same workload."""
+    pw = mi.WORKLOADS[PREFILL_WORKLOAD]
+    res = time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
+                       stream, pw, args.prefill_steps)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on prefill tokens")
+        res["cpu_baseline"] = prefill_cpu_baseline(mi.prefill_inputs(pw), pw)
+    result["prefill"] = res
 
 
 def main():
@@ -604,7 +650,7 @@ def main():
         " p90 %.1f)" % (ms_per_step * 1e3, kern_avg_ms * 1e3, np.percentile(kern_ms, 10) * 1e3,
                         np.percentile(kern_ms, 90) * 1e3))
 
-    ceiling = read_ceiling_gbs(torch, mla, stream, alg_bytes, len(pools))
+    ceiling = read_ceiling_gbs(torch, stream, alg_bytes, len(pools))
     log("plain read of the same %d bytes: %.0f GB/s (best of grids %s)"
         % (alg_bytes, ceiling["gbs"], ceiling["grids"]))
 
@@ -639,7 +685,7 @@ def main():
                                       "frac_of_peak": round(ceiling["gbs"] / HBM_PEAK_GBS, 4),
                                       "achieved_over_ceiling":
                                           round(achieved / ceiling["gbs"], 4),
-                                      "kernel": "read_probe_kernel (mla_hbm_read_probe)"}},
+                                      "kernel": "read_probe_kernel (libmla_read_probe.so)"}},
     }
 
     # ---------------- prefill (the metric's second half) ----------------

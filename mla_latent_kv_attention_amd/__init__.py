@@ -73,8 +73,6 @@ def library() -> ctypes.CDLL:
         lib.mla_top_k_renorm_prob.argtypes = [P, P, I, I, P, P, Z, P]
         lib.mla_top_k_renorm_workspace_size.restype = Z
         lib.mla_top_k_renorm_workspace_size.argtypes = [I, I]
-        lib.mla_hbm_read_probe.restype = I
-        lib.mla_hbm_read_probe.argtypes = [P, Z, P, I, P]
         lib.mla_status_string.restype = ctypes.c_char_p
         lib.mla_status_string.argtypes = [I]
         lib.mla_version.restype = I
@@ -118,6 +116,37 @@ def _dev_i32(t: Optional[torch.Tensor], name: str, dev: torch.device):
     if t.dtype != torch.int32 or t.device != dev or not t.is_contiguous():
         raise TypeError("%s must be a contiguous int32 tensor on %s" % (name, dev))
     return t
+
+
+def _out_buffer(t: Optional[torch.Tensor], name: str, shape, dtype: torch.dtype,
+                dev: torch.device) -> Optional[torch.Tensor]:
+    """A caller-supplied output buffer must be exactly what the kernels write: contiguous,
+    on the inputs' device, of the stated shape and dtype (a smaller or narrower buffer
+    would be written past its end)."""
+    if t is None:
+        return None
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != dev
+            or not t.is_contiguous()):
+        raise TypeError("%s must be a contiguous %s tensor of shape %s on %s (got %s %s on %s%s)"
+                        % (name, dtype, tuple(shape), dev, t.dtype, tuple(t.shape), t.device,
+                           "" if t.is_contiguous() else ", not contiguous"))
+    return t
+
+
+def _workspace_buffer(t: Optional[torch.Tensor], dev: torch.device) -> Optional[torch.Tensor]:
+    if t is None:
+        return None
+    if t.dtype != torch.uint8 or t.device != dev or not t.is_contiguous():
+        raise TypeError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    return t
+
+
+def _check_batch_arrays(B: int, block_table, seq_lens, kv_begin, kv_end):
+    if block_table.dim() != 2 or block_table.shape[0] != B or block_table.shape[1] < 1:
+        raise TypeError("block_table must be [B, max_blocks_per_seq] with B = %d" % B)
+    for name, t in (("seq_lens", seq_lens), ("kv_begin", kv_begin), ("kv_end", kv_end)):
+        if t is not None and tuple(t.shape) != (B,):
+            raise TypeError("%s must be [B] with B = %d" % (name, B))
 
 
 def decode_num_splits(B: int, P: int, H: int, max_kv_len: int, num_splits: int = 0,
@@ -175,11 +204,15 @@ def verify(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
     seq_lens = _dev_i32(seq_lens, "seq_lens", dev)
     kv_begin = _dev_i32(kv_begin, "kv_begin", dev)
     kv_end = _dev_i32(kv_end, "kv_end", dev)
+    _check_batch_arrays(B, block_table, seq_lens, kv_begin, kv_end)
+    od = _out_dtype(out_dtype)
+    out = _out_buffer(out, "out", (B, P, H, HEAD_DIM_V), out_dtype, dev)
+    lse = _out_buffer(lse, "lse", (B, P, H), torch.float32, dev)
+    workspace = _workspace_buffer(workspace, dev)
     if max_kv_len is None:
         hi = seq_lens if kv_end is None else torch.minimum(seq_lens, kv_end)
         lo = torch.zeros_like(hi) if kv_begin is None else kv_begin.clamp(min=0)
         max_kv_len = int((hi - lo).clamp(min=0).max().item()) if B > 0 else 0
-    od = _out_dtype(out_dtype)
     if out is None:
         out = torch.empty((B, P, H, HEAD_DIM_V), dtype=out_dtype, device=dev)
     if lse is None and return_lse:
@@ -211,18 +244,29 @@ def verify_launcher(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.
     if q.dim() != 4 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16 or \
             not q.is_contiguous():
         raise TypeError("q must be a contiguous [B, P, H, 576] bfloat16 tensor")
-    if not kv_cache.is_contiguous() or not out.is_contiguous():
-        raise TypeError("kv_cache and out must be contiguous")
     dev = q.device
     B, P, H, _ = q.shape
+    if (kv_cache.dim() != 3 or kv_cache.shape[-1] != HEAD_DIM_K or kv_cache.device != dev
+            or not kv_cache.is_contiguous()):
+        raise TypeError("kv_cache must be a contiguous [num_blocks, block_size, 576] tensor on "
+                        "the query's device")
+    bt = _dev_i32(block_table, "block_table", dev)
+    sl = _dev_i32(seq_lens, "seq_lens", dev)
+    kb = _dev_i32(kv_begin, "kv_begin", dev)
+    ke = _dev_i32(kv_end, "kv_end", dev)
+    _check_batch_arrays(B, bt, sl, kb, ke)
+    if out is None:
+        raise TypeError("out is required")
+    _out_buffer(out, "out", (B, P, H, HEAD_DIM_V), out.dtype, dev)
+    od = _out_dtype(out.dtype)
+    _out_buffer(lse, "lse", (B, P, H), torch.float32, dev)
+    _workspace_buffer(workspace, dev)
     need = lib.mla_decode_workspace_size(B, P, H, int(max_kv_len), int(num_splits))
     if need > 0 and (workspace is None or workspace.numel() < need):
         raise MlaError("mla_verify", -3)
-    args = (_ptr(q), _ptr(kv_cache), _kv_dtype(kv_cache), float(kv_scale),
-            _ptr(_dev_i32(block_table, "block_table", dev)), block_table.shape[1],
-            kv_cache.shape[1], _ptr(_dev_i32(seq_lens, "seq_lens", dev)),
-            _ptr(_dev_i32(kv_begin, "kv_begin", dev)), _ptr(_dev_i32(kv_end, "kv_end", dev)),
-            B, P, H, int(max_kv_len), float(softmax_scale), _ptr(out), _out_dtype(out.dtype),
+    args = (_ptr(q), _ptr(kv_cache), _kv_dtype(kv_cache), float(kv_scale), _ptr(bt),
+            bt.shape[1], kv_cache.shape[1], _ptr(sl), _ptr(kb), _ptr(ke),
+            B, P, H, int(max_kv_len), float(softmax_scale), _ptr(out), od,
             _ptr(lse), int(num_splits), _ptr(workspace),
             0 if workspace is None else workspace.numel())
     fn = lib.mla_verify
@@ -241,6 +285,10 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
         raise TypeError("q must be [B, H, 576]")
     out = kw.pop("out", None)
     lse = kw.pop("lse", None)
+    B, H = q.shape[0], q.shape[1]
+    od = kw.get("out_dtype", torch.float32)
+    _out_buffer(out, "out", (B, H, HEAD_DIM_V), od, q.device)
+    _out_buffer(lse, "lse", (B, H), torch.float32, q.device)
     o, l = verify(q.unsqueeze(1), kv_cache, block_table, seq_lens,
                   out=None if out is None else out.unsqueeze(1),
                   lse=None if lse is None else lse.unsqueeze(1), **kw)
@@ -259,14 +307,18 @@ def prefill(q: torch.Tensor, kv: torch.Tensor, cu_seqlens: torch.Tensor, *,
     dev = q.device
     T, H, _ = q.shape
     q = q.contiguous()
-    kv = kv.contiguous()
-    if kv.shape != (T, HEAD_DIM_K) or kv.device != dev:
+    if tuple(kv.shape) != (T, HEAD_DIM_K) or kv.device != dev:
         raise TypeError("kv must be [T, 576] on the query's device")
+    kv = kv.contiguous()
     cu = _dev_i32(cu_seqlens, "cu_seqlens", dev)
     B = cu.numel() - 1
     if max_seqlen is None:
         max_seqlen = int((cu[1:] - cu[:-1]).max().item()) if B > 0 else 0
+    if cu.dim() != 1 or cu.numel() < 1:
+        raise TypeError("cu_seqlens must be [B + 1]")
     od = _out_dtype(out_dtype)
+    out = _out_buffer(out, "out", (T, H, HEAD_DIM_V), out_dtype, dev)
+    lse = _out_buffer(lse, "lse", (T, H), torch.float32, dev)
     if out is None:
         out = torch.empty((T, H, HEAD_DIM_V), dtype=out_dtype, device=dev)
     if lse is None and return_lse:
@@ -292,7 +344,11 @@ def merge_lse(part_out: torch.Tensor, part_lse: torch.Tensor, *,
     dev = part_out.device
     part_out = part_out.contiguous()
     part_lse = part_lse.contiguous()
+    if part_lse.device != dev:
+        raise TypeError("part_lse must be on part_out's device")
     od = _out_dtype(out_dtype)
+    out = _out_buffer(out, "out", (N, HEAD_DIM_V), out_dtype, dev)
+    lse = _out_buffer(lse, "lse", (N,), torch.float32, dev)
     if out is None:
         out = torch.empty((N, HEAD_DIM_V), dtype=out_dtype, device=dev)
     if lse is None and return_lse:
@@ -364,20 +420,6 @@ def top_k_renorm_prob(probs: torch.Tensor, top_k: torch.Tensor, *,
                                    _ptr(workspace), workspace.numel(), _stream(dev))
     _check("mla_top_k_renorm_prob", st)
     return out
-
-
-def hbm_read_probe(src: torch.Tensor, sink: torch.Tensor, *, grid: int = 1024) -> None:
-    """Launch the plain-read probe over src's bytes (a measurement helper: timed by the
-    caller, it gives the device's rate for a kernel that only reads those bytes).
-    sink: int32 device tensor of at least grid * 256 elements."""
-    if not src.is_contiguous() or src.device.type != "cuda":
-        raise TypeError("src must be a contiguous device tensor")
-    if sink.dtype != torch.int32 or sink.numel() < grid * 256 or sink.device != src.device:
-        raise TypeError("sink must be an int32 tensor of grid * 256 elements on src's device")
-    nbytes = src.numel() * src.element_size()
-    _check("mla_hbm_read_probe",
-           library().mla_hbm_read_probe(_ptr(src), nbytes - nbytes % 16, _ptr(sink), int(grid),
-                                        _stream(src.device)))
 
 
 def default_softmax_scale(qk_dim: int = 192) -> float:

@@ -1,4 +1,6 @@
-"""Build the HIP library libmla.so for gfx950 with hipcc (in-tree)."""
+"""Build the HIP libraries for gfx950 with hipcc (in-tree): libmla.so, the attention
+library behind include/mla.h, and libmla_read_probe.so, the benchmark's plain-read
+probe (a measurement helper kept out of the attention library)."""
 from __future__ import annotations
 
 import os
@@ -9,8 +11,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_prefill.hip", "mla_cache.hip", "mla_sampling.hip",
-           "mla_probe.hip"]
+SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_prefill.hip", "mla_cache.hip", "mla_sampling.hip"]
+PROBE_LIB = os.path.join(PKG, "libmla_read_probe.so")
+PROBE_SOURCES = [os.path.join("probe", "mla_read_probe.hip")]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -22,13 +25,13 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+def _build_one(sources, lib, verbose: bool) -> str:
     srcs = []
-    for s in SOURCES:
+    for s in sources:
         path = os.path.join(CSRC, s)
         srcs += (["-x", "hip"] if s.endswith(".cpp") else []) + [path]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(CSRC, "probe")] + srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -38,8 +41,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile both libraries; returns the attention library's path."""
+    _build_one(PROBE_SOURCES, PROBE_LIB, verbose)
+    return _build_one(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

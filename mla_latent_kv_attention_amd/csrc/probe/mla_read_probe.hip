@@ -1,10 +1,12 @@
-// mla_probe.hip -- the plain-read probe behind mla_hbm_read_probe: the rate at which
-// the device delivers a given number of bytes to a kernel that only reads them.
+// mla_read_probe.hip -- measurement helper, built as its own library (libmla_read_probe.so)
+// next to the attention library: the plain-read probe behind mla_hbm_read_probe, i.e. the
+// rate at which the device delivers a given number of bytes to a kernel that only reads
+// them.  Not part of the attention boundary.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
 
-#include "mla.h"
+#include "mla_read_probe.h"
 
 namespace {
 
@@ -34,14 +36,14 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* __restri
 
 }  // namespace
 
-extern "C" mla_status mla_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink,
-                                         int grid, void* stream) {
-  if (!src || !sink || grid < 1 || grid > 65536) return MLA_E_INVAL;
-  if (bytes % 16 != 0 || ((uintptr_t)src & 15) != 0) return MLA_E_INVAL;
+extern "C" int mla_hbm_read_probe(const void* src, size_t bytes, uint32_t* sink, int grid,
+                                  void* stream) {
+  if (!src || !sink || grid < 1 || grid > 65536) return -1;
+  if (bytes % 16 != 0 || ((uintptr_t)src & 15) != 0) return -1;
   const size_t n16 = bytes / 16;
-  if (n16 == 0) return MLA_OK;
+  if (n16 == 0) return 0;
   const size_t per = (n16 + grid - 1) / grid;
   hipLaunchKernelGGL(read_probe_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                      (const u32x4_t*)src, n16, per, sink);
-  return hipGetLastError() == hipSuccess ? MLA_OK : MLA_E_LAUNCH;
+  return hipGetLastError() == hipSuccess ? 0 : -4;
 }

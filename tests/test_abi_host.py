@@ -209,12 +209,15 @@ def test_explicit_split_count_is_honoured(lib):
     assert lib.mla_decode_num_splits(2, 5, 16, 10, 3, 256) == -2
 
 
-def test_read_probe_rejects_bad_arguments_before_launch(lib):
-    """The measurement helper: null pointers, a size or address not a multiple of 16
-    and grids outside 1 .. 65536 are refused; an empty read launches nothing."""
-    lib.mla_hbm_read_probe.restype = ctypes.c_int
-    lib.mla_hbm_read_probe.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
-                                       ctypes.c_int, ctypes.c_void_p]
+def test_read_probe_rejects_bad_arguments_before_launch():
+    """The benchmark's measurement helper (its own library, not the attention boundary):
+    null pointers, a size or address not a multiple of 16 and grids outside 1 .. 65536
+    are refused; an empty read launches nothing."""
+    from mla_latent_kv_attention_amd import read_probe
+    if not os.path.exists(read_probe.LIB_PATH):
+        from mla_latent_kv_attention_amd import build
+        build.build()
+    lib = read_probe.library()
     P = ctypes.c_void_p(0x1000)
     assert lib.mla_hbm_read_probe(None, 16, P, 1, None) == -1
     assert lib.mla_hbm_read_probe(P, 16, None, 1, None) == -1
@@ -223,3 +226,7 @@ def test_read_probe_rejects_bad_arguments_before_launch(lib):
     assert lib.mla_hbm_read_probe(P, 16, P, 0, None) == -1
     assert lib.mla_hbm_read_probe(P, 16, P, 65537, None) == -1
     assert lib.mla_hbm_read_probe(P, 0, P, 4, None) == 0
+
+
+def test_attention_library_does_not_export_the_probe(lib):
+    assert not hasattr(lib, "mla_hbm_read_probe")

@@ -4,9 +4,9 @@ Small cases (the oracle computes every row) span several 16-token steps, several
 pieces of the batch's step list, ragged tails, partial last blocks, empty key ranges, 8 / 12 / 16 heads, one to
 four query positions, BF16 and FP8 caches, FP32 and BF16 outputs.  The full-size
 workloads run in the launch configuration the bench times (automatic split plan) and
-are checked on every row (decode, 32 sequences) or on sampled rows (long contexts).
-Invariants: piece count, head padding, paging layout, run-to-run determinism, and the
-workspace contract (counters left zero).
+are checked on every row.  Invariants: piece count, head padding and head repetition
+(bitwise), power-of-two scalings of q, the softmax scale and the FP8 scale (bitwise),
+paging layout, run-to-run determinism, and the workspace contract (counters left zero).
 """
 import numpy as np
 import pytest
@@ -184,6 +184,59 @@ def test_zero_padded_heads_are_bitwise_invariant(mla):
     check_lse(l16[:, :, 12:], ref_l[:, :, 12:])
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_repeated_heads_are_bitwise_invariant(mla, kv_dtype):
+    """Head repetition 8 -> 16 (each head's query twice, as a caller that needs 16 heads
+    would feed 8 real ones): both copies of every head come out bitwise equal to the
+    8-head call at the same piece count, whichever 16-row block they land in."""
+    q8, cache = small_case(2015, [900, 2048, 37], 8, 4, kv_dtype)
+    q16 = np.repeat(q8, 2, axis=2)
+    o8, l8 = run_gpu(mla, q8, cache, num_splits=5)
+    o16, l16 = run_gpu(mla, q16, cache, num_splits=5)
+    for c in range(2):
+        assert torch.equal(o16[:, :, c::2], o8) and torch.equal(l16[:, :, c::2], l8)
+    ref_o, ref_l = run_oracle(q8, cache)
+    check_out(o8, ref_o)
+    check_lse(l8, ref_l)
+
+
+def scaled_bf16_bits(bits: np.ndarray, c: float) -> np.ndarray:
+    """BF16 bit patterns multiplied by a power of two c (exact for these magnitudes)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(c)
+    out = mi.to_bf16_bits(f)
+    assert np.array_equal((out.astype(np.uint32) << 16).view(np.float32), f)
+    return out
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("splits", [1, 6, 200])
+def test_power_of_two_scale_invariants(mla, kv_dtype, splits):
+    """Scores depend on q and the softmax scale only through their product, and an FP8
+    cache's values through code x kv_scale: (q * c, scale / c) gives bitwise the same
+    out and lse for a power of two c, and (kv_scale * c, scale / c) gives out * c and the
+    same lse, in every merge form (one piece, shares merged in the launch, the separate
+    merge)."""
+    q, cache = small_case(2016, [700, 1500, 64], 12, 2, kv_dtype)
+    kv, bt, sl = cache_to_device(cache, DEV)
+
+    def run(q_bits, scale, kv_scale):
+        o, l = mla.verify(bf16_tensor(q_bits, DEV), kv, bt, sl, softmax_scale=scale,
+                          kv_scale=kv_scale, num_splits=splits, max_kv_len=1500)
+        torch.cuda.synchronize()
+        return o, l
+    base_o, base_l = run(q, SIGMA, cache.kv_scale)
+    for c in (2.0, 0.25):
+        o, l = run(scaled_bf16_bits(q, c), SIGMA / c, cache.kv_scale)
+        assert torch.equal(o, base_o) and torch.equal(l, base_l)
+    if kv_dtype == "fp8":
+        for c in (4.0, 0.5):
+            o, l = run(q, SIGMA / c, cache.kv_scale * c)
+            assert torch.equal(o, base_o * c) and torch.equal(l, base_l)
+    ref_o, ref_l = run_oracle(q, cache)
+    check_out(base_o, ref_o)
+    check_lse(base_l, ref_l)
+
+
 def test_paging_layout_is_bitwise_invariant(mla):
     lens = [700, 1200]
     q, paged = small_case(2008, lens, 12, 2, "fp8", block_size=64)
@@ -241,12 +294,6 @@ def full_case(name):
     return w, d["q"], d["cache"]
 
 
-def sample_rows(n_total, k, seed):
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, n_total - 1], rng.choice(n_total, k, replace=False)]))
-    return rows.astype(np.int64)
-
-
 def test_full_decode_b1_h12_l1024_bf16(mla):
     w, q, cache = full_case("decode_b1_h12_l1024_bf16")
     print("full", w.name, flush=True)
@@ -273,15 +320,31 @@ def test_full_verify(mla, name):
     print("full", name, flush=True)
     out, lse = run_gpu(mla, q, cache, max_kv_len=32768)
     B, P, H = q.shape[:3]
-    rows = sample_rows(B * P * H, 40, 11)
-    ref_o, ref_l = run_oracle(q, cache, rows=rows)
-    check_out(out.reshape(-1, 512)[torch.from_numpy(rows).to(DEV)], ref_o)
-    check_lse(lse.reshape(-1)[torch.from_numpy(rows).to(DEV)], ref_l)
+    ref_o, ref_l = run_oracle(q, cache)  # every row
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
     if w.pad_heads_to:
         q12 = np.ascontiguousarray(q[:, :, :w.heads])
         S = mla.decode_num_splits(B, P, H, 32768)
         o12, l12 = run_gpu(mla, q12, cache, num_splits=S)
         assert torch.equal(out[:, :, :w.heads], o12) and torch.equal(lse[:, :, :w.heads], l12)
+
+
+def test_full_verify_heads_repeated_8_to_16(mla):
+    """The 8-head verify workload with each head repeated (8 -> 16 heads), at the piece
+    count the automatic plan gives 16 heads: both copies bitwise equal to the 8-head call
+    at that piece count, and the 8-head result matches the oracle on every row."""
+    w, q8, cache = full_case("verify_b4_p4_h8_l32768_bf16")
+    print("full repetition", w.name, flush=True)
+    B, P, H = q8.shape[:3]
+    S = mla.decode_num_splits(B, P, 2 * H, 32768)
+    o16, l16 = run_gpu(mla, np.repeat(q8, 2, axis=2), cache, num_splits=S, max_kv_len=32768)
+    o8, l8 = run_gpu(mla, q8, cache, num_splits=S, max_kv_len=32768)
+    for c in range(2):
+        assert torch.equal(o16[:, :, c::2], o8) and torch.equal(l16[:, :, c::2], l8)
+    ref_o, ref_l = run_oracle(q8, cache)
+    check_out(o8, ref_o)
+    check_lse(l8, ref_l)
 
 
 def test_full_verify_b1_p4_h12_l32768_fp8(mla):
@@ -292,13 +355,11 @@ def test_full_verify_b1_p4_h12_l32768_fp8(mla):
     print("full", w.name, flush=True)
     B, P, H = q.shape[:3]
     assert mla.decode_num_splits(B, P, H, 32768) > 16
-    rows = sample_rows(B * P * H, 30, 13)
-    ref_o, ref_l = run_oracle(q, cache, rows=rows)
-    idx = torch.from_numpy(rows).to(DEV)
+    ref_o, ref_l = run_oracle(q, cache)  # every row
     for splits in [0, 16]:
         out, lse = run_gpu(mla, q, cache, max_kv_len=32768, num_splits=splits)
-        check_out(out.reshape(-1, 512)[idx], ref_o)
-        check_lse(lse.reshape(-1)[idx], ref_l)
+        check_out(out, ref_o)
+        check_lse(lse, ref_l)
 
 
 def test_full_decode_b8_h12_l142000_fp8_8parts(mla):
@@ -319,7 +380,7 @@ def test_full_decode_b8_h12_l142000_fp8_8parts(mla):
     torch.cuda.synchronize()
     assert (mo - whole_o.reshape(-1, 512)).abs().max().item() < 2e-3
     assert (ml - whole_l.reshape(-1)).abs().max().item() < 2e-5
-    rows = sample_rows(B * H, 16, 13)
+    rows = np.arange(B * H, dtype=np.int64)  # every row
     ref_o, ref_l = run_oracle(q, cache, rows=rows)
     idx = torch.from_numpy(rows).to(DEV)
     check_out(mo[idx], ref_o, "merged out")

@@ -11,7 +11,7 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("nbytes,grid", [(16, 1), (4096, 7), (1 << 20, 512), (3 << 20, 2048),
                                          (1000016, 1024)])
 def test_read_probe_reads_every_word_once(nbytes, grid):
-    import mla_latent_kv_attention_amd as mla
+    from mla_latent_kv_attention_amd import read_probe as mla
     rng = np.random.default_rng(nbytes + grid)
     words = rng.integers(0, 2**32, nbytes // 4, dtype=np.uint64).astype(np.uint32)
     src = torch.from_numpy(words.view(np.int32)).to("cuda:0")
