@@ -34,7 +34,8 @@ DTYPE_FP8_E4M3 = 1
 DTYPE_FP32 = 2
 
 _STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported shape or dtype",
-           -3: "workspace missing or too small", -4: "HIP launch or query failed"}
+           -3: "workspace missing or too small", -4: "HIP launch or query failed",
+           -5: "needs more than the no-allocation entry point's scratch"}
 
 
 class MlaError(RuntimeError):
@@ -57,6 +58,9 @@ def library() -> ctypes.CDLL:
         P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
         lib.mla_verify.restype = I
         lib.mla_verify.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, I, F, P, I, P, I, P, Z, P]
+        lib.mla_verify_noalloc.restype = I
+        lib.mla_verify_noalloc.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, I, F, P, I, P, I,
+                                           P]
         lib.mla_decode.restype = I
         lib.mla_decode.argtypes = [P, P, I, F, P, I, I, P, P, P, I, I, I, F, P, I, P, I, P, Z, P]
         lib.mla_prefill.restype = I
@@ -228,6 +232,38 @@ def verify(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
         _stream(dev))
     _check("mla_verify", st)
     return out, lse
+
+
+def verify_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                   seq_lens: torch.Tensor, *, softmax_scale: float, max_kv_len: int,
+                   out: torch.Tensor, lse: Optional[torch.Tensor] = None, kv_scale: float = 1.0,
+                   kv_begin: Optional[torch.Tensor] = None, kv_end: Optional[torch.Tensor] = None,
+                   num_splits: int = 0) -> None:
+    """mla_verify_noalloc: verify into caller-allocated out [B, P, H, 512] (fp32 or bf16) and
+    lse [B, P, H] fp32 (or None), with the library's own per-GPU scratch instead of a
+    workspace.  Allocates nothing on the device.  Calls that overlap on one GPU race."""
+    lib = library()
+    if q.dim() != 4 or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16 or \
+            not q.is_contiguous():
+        raise TypeError("q must be a contiguous [B, P, H, 576] bfloat16 tensor")
+    dev = q.device
+    B, P, H, _ = q.shape
+    if (kv_cache.dim() != 3 or kv_cache.shape[-1] != HEAD_DIM_K or kv_cache.device != dev
+            or not kv_cache.is_contiguous()):
+        raise TypeError("kv_cache must be a contiguous [num_blocks, block_size, 576] tensor on "
+                        "the query's device")
+    bt = _dev_i32(block_table, "block_table", dev)
+    sl = _dev_i32(seq_lens, "seq_lens", dev)
+    kb = _dev_i32(kv_begin, "kv_begin", dev)
+    ke = _dev_i32(kv_end, "kv_end", dev)
+    _check_batch_arrays(B, bt, sl, kb, ke)
+    _out_buffer(out, "out", (B, P, H, HEAD_DIM_V), out.dtype, dev)
+    od = _out_dtype(out.dtype)
+    _out_buffer(lse, "lse", (B, P, H), torch.float32, dev)
+    _check("mla_verify_noalloc", lib.mla_verify_noalloc(
+        _ptr(q), _ptr(kv_cache), _kv_dtype(kv_cache), float(kv_scale), _ptr(bt), bt.shape[1],
+        kv_cache.shape[1], _ptr(sl), _ptr(kb), _ptr(ke), B, P, H, int(max_kv_len),
+        float(softmax_scale), _ptr(out), od, _ptr(lse), int(num_splits), _stream(dev)))
 
 
 def verify_launcher(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,

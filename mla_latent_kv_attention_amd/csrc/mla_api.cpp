@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "mla.h"
 #include "mla_kernels.h"
@@ -108,6 +109,9 @@ const char* mla_status_string(int status) {
     case MLA_E_UNSUPPORTED: return "unsupported shape or dtype";
     case MLA_E_WORKSPACE: return "workspace missing or too small";
     case MLA_E_LAUNCH: return "HIP launch or query failed";
+    case MLA_E_TOO_LARGE:
+      return "the call needs more scratch than mla_verify_noalloc holds "
+             "(MLA_NOALLOC_SCRATCH_BYTES); use mla_verify with a workspace";
     default: return "unknown status";
   }
 }
@@ -172,6 +176,68 @@ mla_status setup_decode(const void* q, const void* kv_cache, int kv_dtype, float
   return MLA_OK;
 }
 
+// Carve the workspace, then launch the decode kernel (and the separate merge when the
+// plan needs it).  clear_counters: zero the counters the call uses first (a fill kernel
+// on the same stream), for a workspace whose counters a caller cannot vouch for.
+mla_status launch_verify(mla_impl::DecodeParams& p, const Plan& pl, int kv_dtype, void* out,
+                         int out_dtype, float* lse, void* workspace, bool clear_counters,
+                         hipStream_t stm) {
+  p.out = out;
+  p.out_bf16 = out_dtype == MLA_DTYPE_BF16;
+  p.lse = lse;
+  if (pl.W > 1) {
+    const size_t rows = (size_t)(pl.W + p.B) * pl.R;
+    char* ws = static_cast<char*>(workspace);
+    p.counters = reinterpret_cast<int*>(ws);
+    ws += kCounterBytes;
+    p.part_out = reinterpret_cast<float*>(ws);
+    ws += align_up(rows * MLA_HEAD_DIM_V * sizeof(float));
+    p.part_lse = reinterpret_cast<float*>(ws);
+    ws += align_up(rows * sizeof(float));
+    p.seq_pieces = reinterpret_cast<int*>(ws);
+    p.merge_in_kernel = pl.merge_in_kernel ? 1 : 0;
+    if (clear_counters && p.merge_in_kernel &&
+        mla_impl::launch_clear_i32(p.counters, (long)p.B * pl.RB, stm) != hipSuccess)
+      return MLA_E_LAUNCH;
+  } else {
+    p.merge_in_kernel = 1;  // one piece: every sequence is written whole
+  }
+  const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
+  if (mla_impl::launch_decode(p, fp8, stm) != hipSuccess) return MLA_E_LAUNCH;
+  if (!p.merge_in_kernel && mla_impl::launch_merge_shares(p, stm) != hipSuccess)
+    return MLA_E_LAUNCH;
+  return MLA_OK;
+}
+
+// ---- the entry point that allocates nothing (its scratch array is below) ----
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+
+}  // namespace
+
+// The workspace of mla_verify_noalloc: one copy per GPU, zero when the code object
+// loads, held until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it only stands for the symbol); it passes the per-device address
+// hipGetSymbolAddress returns, looked up once per device on the first call.
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of this device's copy of `scratch`, or nullptr if the runtime refuses.
+void* scratch_for_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 mla_status mla_verify(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
@@ -191,29 +257,8 @@ mla_status mla_verify(const void* q, const void* kv_cache, int kv_dtype, float k
   if (B == 0) return MLA_OK;
   const size_t need = workspace_bytes_for(pl, B);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_E_WORKSPACE;
-  p.out = out;
-  p.out_bf16 = out_dtype == MLA_DTYPE_BF16;
-  p.lse = lse;
-  if (pl.W > 1) {
-    const size_t rows = (size_t)(pl.W + B) * pl.R;
-    char* ws = static_cast<char*>(workspace);
-    p.counters = reinterpret_cast<int*>(ws);
-    ws += kCounterBytes;
-    p.part_out = reinterpret_cast<float*>(ws);
-    ws += align_up(rows * MLA_HEAD_DIM_V * sizeof(float));
-    p.part_lse = reinterpret_cast<float*>(ws);
-    ws += align_up(rows * sizeof(float));
-    p.seq_pieces = reinterpret_cast<int*>(ws);
-    p.merge_in_kernel = pl.merge_in_kernel ? 1 : 0;
-  } else {
-    p.merge_in_kernel = 1;  // one piece: every sequence is written whole
-  }
-  const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
-  const hipStream_t stm = static_cast<hipStream_t>(stream);
-  if (mla_impl::launch_decode(p, fp8, stm) != hipSuccess) return MLA_E_LAUNCH;
-  if (!p.merge_in_kernel && mla_impl::launch_merge_shares(p, stm) != hipSuccess)
-    return MLA_E_LAUNCH;
-  return MLA_OK;
+  return launch_verify(p, pl, kv_dtype, out, out_dtype, lse, workspace, false,
+                       static_cast<hipStream_t>(stream));
 }
 
 mla_status mla_decode(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
@@ -225,6 +270,29 @@ mla_status mla_decode(const void* q, const void* kv_cache, int kv_dtype, float k
   return mla_verify(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
                     block_size, seq_lens, kv_begin, kv_end, B, 1, H, max_kv_len, softmax_scale,
                     out, out_dtype, lse, num_splits, workspace, workspace_bytes, stream);
+}
+
+mla_status mla_verify_noalloc(const void* q, const void* kv_cache, int kv_dtype,
+                              float kv_scale, const int32_t* block_table,
+                              int max_blocks_per_seq, int block_size, const int32_t* seq_lens,
+                              const int32_t* kv_begin, const int32_t* kv_end, int B, int P,
+                              int H, int max_kv_len, float softmax_scale, void* out,
+                              int out_dtype, float* lse, int num_splits, void* stream) {
+  if (check_dtype_out(out_dtype) != MLA_OK) return MLA_E_UNSUPPORTED;
+  if (B > 0 && !out) return MLA_E_INVAL;
+  mla_impl::DecodeParams p;
+  Plan pl;
+  mla_status st = setup_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
+                               block_size, seq_lens, kv_begin, kv_end, B, P, H, max_kv_len,
+                               softmax_scale, num_splits, &p, &pl);
+  if (st != MLA_OK) return st;
+  if (B == 0) return MLA_OK;
+  const size_t need = workspace_bytes_for(pl, B);
+  if (need > kScratchBytes) return MLA_E_TOO_LARGE;
+  void* ws = nullptr;
+  if (need > 0 && !(ws = scratch_for_current_device())) return MLA_E_LAUNCH;
+  return launch_verify(p, pl, kv_dtype, out, out_dtype, lse, ws, true,
+                       static_cast<hipStream_t>(stream));
 }
 
 mla_status mla_merge_lse(const float* part_out, const float* part_lse, int S, int N, void* out,

@@ -806,9 +806,22 @@ __global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ pa
   if (lse && threadIdx.x == 0) lse[n] = (mx == -INFINITY) ? -INFINITY : mx + logf(L);
 }
 
+__global__ __launch_bounds__(256) void clear_i32_kernel(int* p, long n) {
+  const long i = (long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 }  // namespace
 
 int decode_grid_size(int W, int RB) { return W * RB; }
+
+hipError_t launch_clear_i32(int* p, long n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const long groups = (n + 255) / 256;
+  if (groups > 0x7fffffffL) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(clear_i32_kernel, dim3((unsigned)groups), dim3(256), 0, stream, p, n);
+  return hipGetLastError();
+}
 
 hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream) {
   const int grid = decode_grid_size(p.W, p.RB);

@@ -41,6 +41,9 @@ int decode_grid_size(int W, int RB);
 
 hipError_t launch_decode(const DecodeParams& p, bool kv_fp8, hipStream_t stream);
 
+// Zero n int32 values at p with a fill kernel (no memset node under graph capture).
+hipError_t launch_clear_i32(int* p, long n, hipStream_t stream);
+
 // The separate merge of a launch_decode with merge_in_kernel = 0 (same params).
 hipError_t launch_merge_shares(const DecodeParams& p, hipStream_t stream);
 

@@ -89,6 +89,20 @@ def test_verify_rejects_bad_arguments_before_launch(lib, over, status):
     assert lib.mla_verify(*verify_args(**over)) == status
 
 
+@pytest.mark.parametrize("over,status", [
+    (dict(P=0), -1), (dict(H=0), -1), (dict(B=-1), -1), (dict(P=5, H=16), -2),
+    (dict(kv_dtype=7), -2), (dict(out_dtype=1), -2), (dict(block_size=24), -1),
+    (dict(kv_dtype=1, kv_scale=0.0), -1), (dict(out=None), -1),
+])
+def test_noalloc_verify_rejects_bad_arguments_before_launch(lib, over, status):
+    """mla_verify_noalloc takes mla_verify's arguments minus the workspace and checks them
+    the same way, before any launch."""
+    a = verify_args(**over)
+    args = a[:19] + [a[21]]  # drop workspace and workspace_bytes
+    lib.mla_verify_noalloc.restype = ctypes.c_int
+    assert lib.mla_verify_noalloc(*args) == status
+
+
 def test_empty_batch_is_a_no_op(lib):
     assert lib.mla_verify(*verify_args(B=0, q=None, kv=None, bt=None, sl=None, out=None)) == 0
 
