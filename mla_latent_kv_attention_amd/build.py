@@ -11,7 +11,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmla.so")
-SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_prefill.hip", "mla_cache.hip", "mla_sampling.hip"]
+SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_verify.hip", "mla_prefill.hip", "mla_cache.hip",
+           "mla_sampling.hip"]
 PROBE_LIB = os.path.join(PKG, "libmla_read_probe.so")
 PROBE_SOURCES = [os.path.join("probe", "mla_read_probe.hip")]
 

@@ -43,7 +43,22 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Plan {
   int R, RB, W;
   bool merge_in_kernel;  // few enough shares per sequence for the last piece to merge them
+  bool shared;           // one work-group per piece for all row blocks (launch_verify_shared)
 };
+
+// Sequences of more than 16 query rows take the kernel whose work-group serves all of a
+// piece's row blocks (each latent row read once per piece) when the batch's key range is
+// long, where streaming dominates: 4 sequences x 4 positions x 32,768 keys, 12 heads:
+// 54.6 us against 64.4 us with one work-group per row block, 16 heads 62.9 against 84.
+// Shorter batches keep one work-group per (piece, row block): there the shares the
+// pieces publish (one fp32 row per query row and piece) outweigh the keys once a piece
+// serves all row blocks of a 256-piece plan (one 32,768-key FP8 sequence x 4 positions:
+// 32.1 us against 23.8 us).
+constexpr long kSharedMinTokens = 65536;  // batch x longest key range
+
+bool use_shared(int B, int RB, int max_kv_len) {
+  return RB >= 2 && (long)(B > 0 ? B : 1) * max_kv_len >= kSharedMinTokens;
+}
 
 // Piece plan.  The kernel is persistent: W pieces x RB row blocks work-groups,
 // one per CU (a work-group's LDS keeps it alone on its CU), each streaming an
@@ -54,14 +69,16 @@ Plan make_plan(int B, int P, int H, int max_kv_len, int num_splits, int cus) {
   Plan pl;
   pl.R = P * H;
   pl.RB = (pl.R + 15) / 16;
+  pl.shared = use_shared(B, pl.RB, max_kv_len);
   const long Bn = B > 0 ? B : 1;
   if (num_splits > 0) {
     pl.W = num_splits < kMaxPieces ? num_splits : kMaxPieces;
     pl.merge_in_kernel = pl.W <= kMaxPiecesPerSeq * Bn;
     return pl;
   }
-  // one work-group per CU (the grid is W x RB), so no piece waits for a CU to free up
-  long W = (cus > 0 ? cus : 256) / pl.RB;
+  // one work-group per CU, so no piece waits for a CU to free up: the grid is W x RB
+  // work-groups with one per (piece, row block), W with one per piece (shared)
+  long W = (cus > 0 ? cus : 256) / (pl.shared ? 1 : pl.RB);
   const long steps = Bn * (((long)max_kv_len + kStepTokens - 1) / kStepTokens);
   const long by_steps = (steps + kMinStepsPerPiece - 1) / kMinStepsPerPiece;
   if (W > by_steps) W = by_steps;
@@ -203,7 +220,9 @@ mla_status launch_verify(mla_impl::DecodeParams& p, const Plan& pl, int kv_dtype
     p.merge_in_kernel = 1;  // one piece: every sequence is written whole
   }
   const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
-  if (mla_impl::launch_decode(p, fp8, stm) != hipSuccess) return MLA_E_LAUNCH;
+  const hipError_t e = pl.shared ? mla_impl::launch_verify_shared(p, fp8, stm)
+                                 : mla_impl::launch_decode(p, fp8, stm);
+  if (e != hipSuccess) return MLA_E_LAUNCH;
   if (!p.merge_in_kernel && mla_impl::launch_merge_shares(p, stm) != hipSuccess)
     return MLA_E_LAUNCH;
   return MLA_OK;

@@ -177,6 +177,41 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
   return v + (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
 }
 
+// One 16-byte global -> LDS copy per lane, no VGPR staging: lane l reads base + voff
+// (base uniform, voff per lane) and lands at LDS byte lds_base + 16 l.  Issued through
+// asm so that the compiler does not fence every later LDS read behind all outstanding
+// loads (it would put a full vmcnt(0) before each); the caller waits for its own copies
+// with explicit vmcnt waits and a barrier.  The LDS base goes in M0 as an operand of the
+// asm ("{m0}"), so the compiler sets M0 itself and knows the asm reads it: nothing
+// writes M0 behind its back.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(base), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// The same copy from a full 64-bit address per lane.
+__device__ __forceinline__ void dma16_addr(const void* src, uint32_t lds_base) {
+  asm volatile("global_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "{m0}"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits 3:0,
+// vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their no-wait maxima).
+template <int kN>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(kN >= 0 && kN < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -36,6 +36,10 @@ struct DecodeParams {
   float* lse;                  // [B * R] or null
 };
 
+// The same for sequences of 2 to 4 row blocks: one work-group per piece serves them all
+// (grid W), each latent row read once per piece and staged in LDS.
+hipError_t launch_verify_shared(const DecodeParams& p, bool kv_fp8, hipStream_t stream);
+
 // Work-groups launch_decode uses for W pieces and RB row blocks.
 int decode_grid_size(int W, int RB);
 

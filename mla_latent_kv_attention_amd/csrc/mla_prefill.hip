@@ -52,29 +52,6 @@ constexpr int kVAhead = 3;     // V^T operands read this many value MFMAs ahead
 static_assert(kTile * kPRowChunks <= kDmaBlocks * 64, "DMA slots must cover a tile");
 static_assert(4 * kDmaPerWave >= kDmaBlocks, "the waves' copies must cover every block");
 
-// One 16-byte global -> LDS copy per lane, no VGPR staging: lane l reads
-// base + voff and lands at LDS byte lds_base + 16 l.  Issued through asm so the
-// compiler does not fence every later LDS read behind all outstanding loads; the
-// kernel waits for its own copies with explicit vmcnt waits and a barrier.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t voff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-               : "memory", "m0");
-}
-
-// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits 3:0,
-// vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at their no-wait maxima).
-template <int kN>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(kN >= 0 && kN < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((kN & 15) | ((kN >> 4) << 14) | (7 << 4) | (15 << 8));
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-}
-
 // Copy key tile [tok0, tok0 + 32) of a sequence into an LDS slot laid out as
 // 32 padded rows of 73 chunks.  Chunk positions past the tile land in the slot's
 // slack; pad chunks and rows past the sequence end get real (masked) rows.

@@ -164,7 +164,8 @@ def test_prefill_rejects_bad_arguments(lib):
 def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
     """The pages' short verify: one sequence, 4 positions, 12 heads; 48 work-groups were
     too few for the chip.  The persistent plan launches more than that, never more than
-    one per CU, once the history is long enough."""
+    one per CU, once the history is long enough.  One work-group serves all of a piece's
+    row blocks, so the grid is the piece count."""
     g = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_closed_forms.json")))
     sv = g["short_verify_workgroups"]
     heads = sv["heads"]
@@ -175,24 +176,29 @@ def test_planner_fills_the_chip_for_the_short_verify_shape(lib):
     for cus in [256, 304]:
         for ctx in [16384, 32768, 142000]:
             W = lib.mla_decode_num_splits(1, 4, heads, ctx, 0, cus)
-            assert W * row_blocks <= cus
-            assert W * row_blocks > sv["wide_tile_workgroups"]
+            grid = W if ctx >= 65536 else W * row_blocks  # one work-group per piece / per row block
+            assert grid <= cus
+            assert grid > sv["wide_tile_workgroups"]
 
 
 @pytest.mark.parametrize("B,P,H,L", [(1, 1, 12, 1024), (32, 1, 12, 16384), (4, 4, 12, 32768),
                                      (4, 4, 16, 32768), (8, 1, 12, 17750), (3, 2, 8, 64),
-                                     (1, 1, 12, 16), (0, 1, 12, 0)])
+                                     (1, 1, 12, 16), (0, 1, 12, 0), (1, 4, 12, 32768),
+                                     (2, 4, 12, 32768), (1, 4, 12, 65536)])
 def test_planner_pieces_fit_the_chip_and_the_work(lib, B, P, H, L):
-    """At most one work-group per CU (the grid is pieces x row blocks), at least two
-    16-token steps per piece (as far as the max_kv_len hint tells), and as many pieces
-    as both allow."""
+    """At most one work-group per CU, at least two 16-token steps per piece (as far as the
+    max_kv_len hint tells), and as many pieces as both allow.  The grid is one work-group
+    per (piece, 16-row block), or one per piece for sequences of several row blocks over
+    a batch key range of at least 65,536 tokens (one work-group serves all row blocks)."""
     RB = -(-(P * H) // 16)
+    shared = RB >= 2 and max(B, 1) * L >= 65536
     for cus in [80, 256, 304]:
         W = lib.mla_decode_num_splits(B, P, H, L, 0, cus)
         steps = max(B, 1) * (-(-L // 16))
-        want = max(1, min(cus // RB, -(-steps // 2)))
+        per_piece = 1 if shared else RB
+        want = max(1, min(cus // per_piece, -(-steps // 2)))
         assert W == want
-        assert W * RB <= cus
+        assert W * per_piece <= cus
 
 
 @pytest.mark.parametrize("B,P,H,L,S", [(32, 1, 12, 16384, 0), (4, 4, 12, 32768, 0),
