@@ -163,6 +163,48 @@ def decode_workspace_size(B: int, P: int, H: int, max_kv_len: int, num_splits: i
     return library().mla_decode_workspace_size(B, P, H, max_kv_len, num_splits)
 
 
+# The decode workspace's error-flags word (after its 65,536 completion counters) and its
+# bits (include/mla.h: MLA_WORKSPACE_FLAGS_OFFSET, MLA_FLAG_*).
+WORKSPACE_FLAGS_OFFSET = 4 * 65536
+FLAG_STALE_COUNTERS = 1
+FLAG_BAD_LENGTHS = 2
+
+
+class WorkspaceError(RuntimeError):
+    """A decode workspace reported error flags (its calls' results are not to be trusted)."""
+
+    def __init__(self, flags: int):
+        what = []
+        if flags & FLAG_STALE_COUNTERS:
+            what.append("completion counters were not zero when a call started (a call did not "
+                        "complete, or calls overlapped on this workspace)")
+        if flags & FLAG_BAD_LENGTHS:
+            what.append("a sequence length or kv_begin outside the contract")
+        super().__init__("decode workspace flags 0x%x: %s" % (flags, "; ".join(what) or "?"))
+        self.flags = flags
+
+
+def decode_workspace_flags(workspace: torch.Tensor) -> int:
+    """The error flags the kernels ORed into a decode workspace (reads device memory:
+    waits for the calls queued on the tensor's stream)."""
+    w = workspace[WORKSPACE_FLAGS_OFFSET:WORKSPACE_FLAGS_OFFSET + 4]
+    return int(w.view(torch.int32).item()) if w.numel() == 4 else 0
+
+
+def reset_decode_workspace(workspace: torch.Tensor) -> None:
+    """Zero a decode workspace's completion counters and error flags."""
+    workspace[:WORKSPACE_FLAGS_OFFSET + 4].zero_()
+
+
+def check_decode_workspace(workspace: torch.Tensor) -> None:
+    """Raise WorkspaceError if the calls on this workspace reported error flags, after
+    zeroing its counters and flags so that the next call starts clean."""
+    flags = decode_workspace_flags(workspace)
+    if flags:
+        reset_decode_workspace(workspace)
+        raise WorkspaceError(flags)
+
+
 # Zero-filled decode workspaces, one per (device, stream): every call leaves the
 # workspace's counters zero, so calls ordered on one stream can share it.
 _workspaces = {}

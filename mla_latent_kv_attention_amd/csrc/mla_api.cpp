@@ -96,11 +96,12 @@ Plan make_plan(int B, int P, int H, int max_kv_len, int num_splits, int cus) {
   return pl;
 }
 
-// Workspace: a fixed block of completion counters at offset 0 (its place and size do
-// not depend on the call's shape, so a workspace that calls of any shape leave zero
-// stays zero there), then the partial rows and lse of the (W + B) slots.  One piece
-// needs none.
-constexpr size_t kCounterBytes = (size_t)MLA_MAX_COUNTERS * sizeof(int);
+// Workspace: a fixed block of completion counters at offset 0 and the error-flags word
+// after it (their place and size do not depend on the call's shape, so a workspace that
+// calls of any shape leave zero stays zero there), then the partial rows and lse of the
+// (W + B) slots.  One piece needs none.
+constexpr size_t kCounterBytes = (size_t)MLA_MAX_COUNTERS * sizeof(int) + kAlign;  // + flags
+static_assert(MLA_WORKSPACE_FLAGS_OFFSET == MLA_MAX_COUNTERS * sizeof(int), "flags word");
 
 size_t workspace_bytes_for(const Plan& pl, int B) {
   if (pl.W <= 1) return 0;
@@ -206,6 +207,8 @@ mla_status launch_verify(mla_impl::DecodeParams& p, const Plan& pl, int kv_dtype
     const size_t rows = (size_t)(pl.W + p.B) * pl.R;
     char* ws = static_cast<char*>(workspace);
     p.counters = reinterpret_cast<int*>(ws);
+    // the no-allocation entry point has nobody to read the flags: none reported
+    p.flags = clear_counters ? nullptr : reinterpret_cast<int*>(ws + MLA_WORKSPACE_FLAGS_OFFSET);
     ws += kCounterBytes;
     p.part_out = reinterpret_cast<float*>(ws);
     ws += align_up(rows * MLA_HEAD_DIM_V * sizeof(float));

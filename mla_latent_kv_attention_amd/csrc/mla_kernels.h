@@ -29,6 +29,7 @@ struct DecodeParams {
   float* part_out;             // [W + B, R, 512]: slot w + b holds piece w's share of sequence b
   float* part_lse;             // [W + B, R]
   int* counters;               // [B, RB] (B * RB <= MLA_MAX_COUNTERS): zero on entry, left zero
+  int* flags;                  // error flags (MLA_FLAG_*), ORed in; null: not reported
   int merge_in_kernel;         // 1: the last piece of a sequence merges; 0: launch_merge_shares
   int* seq_pieces;             // [B, 2]: first and last piece of each sequence (merge_in_kernel 0)
   void* out;                   // [B * R, 512] fp32 or bf16

@@ -118,6 +118,23 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int b, int r
   if (p.lse && j == 0) p.lse[n] = (mx == -INFINITY) ? -INFINITY : mx + logf(ls);
 }
 
+// Error flags (MLA_FLAG_* in mla.h): bits ORed into the workspace's flags word.
+constexpr int kFlagStaleCounters = 1;
+constexpr int kFlagBadLengths = 2;
+
+__device__ __forceinline__ void raise_flag(const DecodeParams& p, int bit) {
+  if (p.flags) __hip_atomic_fetch_or(p.flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Piece 0's check of sequence b's lengths against the stated contract (P <= seq_lens <=
+// max_blocks * block_size, kv_begin >= 0); results are undefined outside it.
+__device__ __forceinline__ void check_lengths(const DecodeParams& p, int b) {
+  const int L = p.seq_lens[b];
+  const bool bad = L < p.P || (long)L > (long)p.max_blocks * p.block_size ||
+                   (p.kv_begin && p.kv_begin[b] < 0);
+  if (bad) raise_flag(p, kFlagBadLengths);
+}
+
 // Sum over the work-group (256 threads); sh holds 4 values and is free on entry.
 __device__ __forceinline__ long long block_sum(long long v, long long* sh) {
 #pragma unroll

@@ -113,6 +113,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       if (b < p.B) sr = seq_range(p, b);
       const long long mb = sr.n > 0 ? sr.n + c : 0;
       if (w == 0 && b < p.B && sr.n == 0) write_empty(b);
+      if (w == 0 && b < p.B) check_lengths(p, b);
       long long incl, tot;
       if (!__builtin_amdgcn_ballot_w64(mb >= (1ll << 25))) {
         const uint32_t i32 = wave_incl_scan((uint32_t)mb);
@@ -149,6 +150,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       const int nb = seq_range(p, b).n;
       part += nb > 0 ? nb + c : 0;
       if (w == 0 && nb == 0) write_empty(b);
+      if (w == 0) check_lengths(p, b);
     }
     if (tid == 0) seg[0] = p.B;
     N = block_sum(part, red);
@@ -522,6 +524,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       int* cnt = p.counters + (size_t)b * p.RB;
       const int done = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const int last = done == w_last - w_first;
+      if (done > w_last - w_first) raise_flag(p, kFlagStaleCounters);  // not zero on entry
       if (last) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last_flag = last;
     }

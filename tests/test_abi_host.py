@@ -204,13 +204,13 @@ def test_planner_pieces_fit_the_chip_and_the_work(lib, B, P, H, L):
 @pytest.mark.parametrize("B,P,H,L,S", [(32, 1, 12, 16384, 0), (4, 4, 12, 32768, 0),
                                        (2, 3, 5, 100, 7), (1, 1, 12, 16, 0)])
 def test_workspace_holds_slots_and_counters(lib, B, P, H, L, S):
-    """A fixed block of 65536 counters first (the same bytes for every shape), then
-    (W + B) x rows partial outputs and lse, then each sequence's piece range, each part
-    256-byte aligned; nothing for a single piece."""
+    """A fixed block of 65536 counters and a 256-byte error-flags block first (the same
+    bytes for every shape), then (W + B) x rows partial outputs and lse, then each
+    sequence's piece range, each part 256-byte aligned; nothing for a single piece."""
     W = lib.mla_decode_num_splits(B, P, H, L, S, 0)  # the plan the workspace query uses
     R = P * H
     al = lambda x: -(-x // 256) * 256
-    want = 0 if W <= 1 else (65536 * 4 + al((W + B) * R * 512 * 4) + al((W + B) * R * 4)
+    want = 0 if W <= 1 else (65536 * 4 + 256 + al((W + B) * R * 512 * 4) + al((W + B) * R * 4)
                              + al(2 * B * 4))
     assert lib.mla_decode_workspace_size(B, P, H, L, S) == want
 

@@ -120,3 +120,33 @@ def test_merge_lse_rejects_mismatched_out_and_lse():
         mla.merge_lse(po, pl, out=torch.zeros((9, 512), dtype=torch.float32))
     with pytest.raises(TypeError, match="lse"):
         mla.merge_lse(po, pl, lse=torch.zeros((10, 2), dtype=torch.float32))
+
+
+def test_workspace_flags_are_read_reported_and_cleared_on_the_host():
+    """The binding's side of the error-flags word: a workspace whose flags word is set
+    raises WorkspaceError naming the cause, and comes back with its counters and flags
+    zeroed; a clean workspace passes."""
+    ws = torch.zeros(mla.WORKSPACE_FLAGS_OFFSET + 4096, dtype=torch.uint8)
+    mla.check_decode_workspace(ws)  # clean
+    ws[:64] = 7                     # stale counters
+    ws[mla.WORKSPACE_FLAGS_OFFSET:mla.WORKSPACE_FLAGS_OFFSET + 4].view(torch.int32)[0] = \
+        mla.FLAG_STALE_COUNTERS | mla.FLAG_BAD_LENGTHS
+    ws[mla.WORKSPACE_FLAGS_OFFSET + 8:] = 9  # partial results: left alone
+    with pytest.raises(mla.WorkspaceError) as e:
+        mla.check_decode_workspace(ws)
+    assert e.value.flags == 3 and "counters" in str(e.value) and "length" in str(e.value)
+    assert torch.all(ws[:mla.WORKSPACE_FLAGS_OFFSET + 4] == 0)
+    assert torch.all(ws[mla.WORKSPACE_FLAGS_OFFSET + 8:] == 9)
+    mla.check_decode_workspace(ws)
+
+
+def test_flags_offset_matches_the_header():
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "include", "mla.h")).read()
+    assert re.search(r"#define MLA_WORKSPACE_FLAGS_OFFSET \(4 \* MLA_MAX_COUNTERS\)", hdr)
+    assert re.search(r"#define MLA_MAX_COUNTERS 65536", hdr)
+    assert re.search(r"#define MLA_FLAG_STALE_COUNTERS 1\b", hdr)
+    assert re.search(r"#define MLA_FLAG_BAD_LENGTHS 2\b", hdr)
+    assert mla.WORKSPACE_FLAGS_OFFSET == 4 * 65536
