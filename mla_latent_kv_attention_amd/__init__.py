@@ -27,7 +27,8 @@ LIB_PATH = os.path.join(_HERE, "libmla.so")
 
 HEAD_DIM_K = 576
 HEAD_DIM_V = 512
-MAX_ROWS = 64
+MAX_ROWS = 64  # query rows per sequence one kernel launch takes; calls group larger P x H
+MAX_CALL_ROWS = 65536  # query rows (P x H) per sequence a decode / verify call accepts
 
 DTYPE_BF16 = 0
 DTYPE_FP8_E4M3 = 1

@@ -116,6 +116,48 @@ mla_status check_dtype_out(int out_dtype) {
   return (out_dtype == MLA_DTYPE_FP32 || out_dtype == MLA_DTYPE_BF16) ? MLA_OK : MLA_E_UNSUPPORTED;
 }
 
+// A sequence's P x H query rows go to the kernels in groups of at most MLA_MAX_ROWS rows,
+// one launch each, every launch reading the sequence's keys again: whole positions
+// (np of them) when the heads fit in a group, otherwise slices of MLA_MAX_ROWS heads of
+// one position.  A group's rows are contiguous within each sequence's rows.
+struct RowGroup {
+  int p0, np;  // positions p0 .. p0 + np - 1
+  int h0, nh;  // heads h0 .. h0 + nh - 1
+};
+
+long row_group_count(int P, int H) {
+  if ((long)P * H <= MLA_MAX_ROWS) return 1;
+  if (H <= MLA_MAX_ROWS) {
+    const int per = MLA_MAX_ROWS / H;
+    return (P + per - 1) / per;
+  }
+  return (long)P * ((H + MLA_MAX_ROWS - 1) / MLA_MAX_ROWS);
+}
+
+RowGroup row_group(int P, int H, long g) {
+  if ((long)P * H <= MLA_MAX_ROWS) return {0, P, 0, H};
+  if (H <= MLA_MAX_ROWS) {
+    const int per = MLA_MAX_ROWS / H;
+    const int p0 = (int)g * per;
+    return {p0, P - p0 < per ? P - p0 : per, 0, H};
+  }
+  const long slices = (H + MLA_MAX_ROWS - 1) / MLA_MAX_ROWS;
+  const int h0 = (int)(g % slices) * MLA_MAX_ROWS;
+  return {(int)(g / slices), 1, h0, H - h0 < MLA_MAX_ROWS ? H - h0 : MLA_MAX_ROWS};
+}
+
+// Groups come in at most two shapes, the first group's and the last's.
+size_t workspace_bytes_all(int B, int P, int H, int max_kv_len, int num_splits, int cus) {
+  const long G = row_group_count(P, H);
+  size_t need = 0;
+  for (long g : {0L, G - 1}) {
+    const RowGroup rg = row_group(P, H, g);
+    const size_t n = workspace_bytes_for(make_plan(B, rg.np, rg.nh, max_kv_len, num_splits, cus), B);
+    if (n > need) need = n;
+  }
+  return need;
+}
+
 }  // namespace
 
 extern "C" {
@@ -139,38 +181,48 @@ int mla_version(void) { return 100; }
 int mla_decode_num_splits(int B, int P, int H, int max_kv_len, int num_splits, int num_cus) {
   if (B < 0 || P < 1 || H < 1 || max_kv_len < 0 || num_splits < 0 || num_cus < 0)
     return MLA_E_INVAL;
-  if ((long)P * H > MLA_MAX_ROWS) return MLA_E_UNSUPPORTED;
+  if ((long)P * H > MLA_MAX_CALL_ROWS) return MLA_E_UNSUPPORTED;
   const int cus = num_cus > 0 ? num_cus : current_cu_count();
-  return make_plan(B, P, H, max_kv_len, num_splits, cus).W;
+  const RowGroup rg = row_group(P, H, 0);
+  return make_plan(B, rg.np, rg.nh, max_kv_len, num_splits, cus).W;
 }
 
 size_t mla_decode_workspace_size(int B, int P, int H, int max_kv_len, int num_splits) {
   if (B < 0 || P < 1 || H < 1 || max_kv_len < 0 || num_splits < 0) return 0;
-  if ((long)P * H > MLA_MAX_ROWS) return 0;
-  return workspace_bytes_for(make_plan(B, P, H, max_kv_len, num_splits, current_cu_count()), B);
+  if ((long)P * H > MLA_MAX_CALL_ROWS) return 0;
+  return workspace_bytes_all(B, P, H, max_kv_len, num_splits, current_cu_count());
 }
 
 namespace {
 
-// Argument checks and parameter setup of mla_verify.
-mla_status setup_decode(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
+// Argument checks of mla_verify, for the whole call (before anything is launched).
+mla_status check_decode(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
                         const int32_t* block_table, int max_blocks_per_seq, int block_size,
-                        const int32_t* seq_lens, const int32_t* kv_begin, const int32_t* kv_end,
-                        int B, int P, int H, int max_kv_len, float softmax_scale,
-                        int num_splits, mla_impl::DecodeParams* p, Plan* pl) {
+                        const int32_t* seq_lens, int B, int P, int H, int max_kv_len,
+                        float softmax_scale, int num_splits) {
   if (B < 0 || P < 1 || H < 1 || max_kv_len < 0 || num_splits < 0) return MLA_E_INVAL;
   if (kv_dtype != MLA_DTYPE_BF16 && kv_dtype != MLA_DTYPE_FP8_E4M3) return MLA_E_UNSUPPORTED;
-  if ((long)P * H > MLA_MAX_ROWS) return MLA_E_UNSUPPORTED;
+  if ((long)P * H > MLA_MAX_CALL_ROWS) return MLA_E_UNSUPPORTED;
   if (block_size <= 0 || block_size % 16 != 0 || max_blocks_per_seq < 1) return MLA_E_INVAL;
   if (!std::isfinite(softmax_scale)) return MLA_E_INVAL;
   if (kv_dtype == MLA_DTYPE_FP8_E4M3 && !finite_positive(kv_scale)) return MLA_E_INVAL;
   if (B > 0 && (!q || !kv_cache || !block_table || !seq_lens)) return MLA_E_INVAL;
   // more sequences x row blocks than counters: only the single-piece plan (no workspace)
-  if ((long)B * ((P * H + 15) / 16) > MLA_MAX_COUNTERS && num_splits != 1)
+  const RowGroup g0 = row_group(P, H, 0);  // the largest group
+  if ((long)B * ((g0.np * g0.nh + 15) / 16) > MLA_MAX_COUNTERS && num_splits != 1)
     return MLA_E_UNSUPPORTED;
+  if (B > 0 && current_cu_count() <= 0) return MLA_E_LAUNCH;
+  return MLA_OK;
+}
+
+// Parameters of the launch over row group rg of a checked call.
+void setup_decode(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
+                  const int32_t* block_table, int max_blocks_per_seq, int block_size,
+                  const int32_t* seq_lens, const int32_t* kv_begin, const int32_t* kv_end,
+                  int B, int P, int H, const RowGroup& rg, int max_kv_len, float softmax_scale,
+                  int num_splits, mla_impl::DecodeParams* p, Plan* pl) {
   const int cus = B > 0 ? current_cu_count() : 256;
-  if (cus <= 0) return MLA_E_LAUNCH;
-  *pl = make_plan(B, P, H, max_kv_len, num_splits, cus);
+  *pl = make_plan(B, rg.np, rg.nh, max_kv_len, num_splits, cus);
   const bool fp8 = kv_dtype == MLA_DTYPE_FP8_E4M3;
   const float kvs = fp8 ? kv_scale : 1.f;
   *p = mla_impl::DecodeParams{};
@@ -183,15 +235,17 @@ mla_status setup_decode(const void* q, const void* kv_cache, int kv_dtype, float
   p->max_blocks = max_blocks_per_seq;
   p->block_size = block_size;
   p->B = B;
-  p->P = P;
-  p->H = H;
+  p->P = rg.np;
+  p->H = rg.nh;
   p->R = pl->R;
   p->RB = pl->RB;
+  p->r_stride = P * H;
+  p->r_off = rg.p0 * H + rg.h0;
+  p->len_shift = P - rg.p0 - rg.np;
   p->W = pl->W;
   p->seg_steps = kv_dtype == MLA_DTYPE_FP8_E4M3 ? kSegmentStepsFp8 : kSegmentStepsBf16;
   p->score_scale_log2 = softmax_scale * kvs * 1.4426950408889634f;
   p->out_scale = kvs;
-  return MLA_OK;
 }
 
 // Carve the workspace, then launch the decode kernel (and the separate merge when the
@@ -270,17 +324,25 @@ mla_status mla_verify(const void* q, const void* kv_cache, int kv_dtype, float k
                       size_t workspace_bytes, void* stream) {
   if (check_dtype_out(out_dtype) != MLA_OK) return MLA_E_UNSUPPORTED;
   if (B > 0 && !out) return MLA_E_INVAL;
-  mla_impl::DecodeParams p;
-  Plan pl;
-  mla_status st = setup_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
-                               block_size, seq_lens, kv_begin, kv_end, B, P, H, max_kv_len,
-                               softmax_scale, num_splits, &p, &pl);
+  mla_status st = check_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
+                               block_size, seq_lens, B, P, H, max_kv_len, softmax_scale,
+                               num_splits);
   if (st != MLA_OK) return st;
   if (B == 0) return MLA_OK;
-  const size_t need = workspace_bytes_for(pl, B);
+  const size_t need = workspace_bytes_all(B, P, H, max_kv_len, num_splits, current_cu_count());
   if (need > 0 && (!workspace || workspace_bytes < need)) return MLA_E_WORKSPACE;
-  return launch_verify(p, pl, kv_dtype, out, out_dtype, lse, workspace, false,
+  // row groups one after another on the stream, each leaving the counters zero
+  for (long g = 0, G = row_group_count(P, H); g < G; ++g) {
+    mla_impl::DecodeParams p;
+    Plan pl;
+    setup_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq, block_size,
+                 seq_lens, kv_begin, kv_end, B, P, H, row_group(P, H, g), max_kv_len,
+                 softmax_scale, num_splits, &p, &pl);
+    st = launch_verify(p, pl, kv_dtype, out, out_dtype, lse, workspace, false,
                        static_cast<hipStream_t>(stream));
+    if (st != MLA_OK) return st;
+  }
+  return MLA_OK;
 }
 
 mla_status mla_decode(const void* q, const void* kv_cache, int kv_dtype, float kv_scale,
@@ -302,19 +364,26 @@ mla_status mla_verify_noalloc(const void* q, const void* kv_cache, int kv_dtype,
                               int out_dtype, float* lse, int num_splits, void* stream) {
   if (check_dtype_out(out_dtype) != MLA_OK) return MLA_E_UNSUPPORTED;
   if (B > 0 && !out) return MLA_E_INVAL;
-  mla_impl::DecodeParams p;
-  Plan pl;
-  mla_status st = setup_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
-                               block_size, seq_lens, kv_begin, kv_end, B, P, H, max_kv_len,
-                               softmax_scale, num_splits, &p, &pl);
+  mla_status st = check_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq,
+                               block_size, seq_lens, B, P, H, max_kv_len, softmax_scale,
+                               num_splits);
   if (st != MLA_OK) return st;
   if (B == 0) return MLA_OK;
-  const size_t need = workspace_bytes_for(pl, B);
+  const size_t need = workspace_bytes_all(B, P, H, max_kv_len, num_splits, current_cu_count());
   if (need > kScratchBytes) return MLA_E_TOO_LARGE;
   void* ws = nullptr;
   if (need > 0 && !(ws = scratch_for_current_device())) return MLA_E_LAUNCH;
-  return launch_verify(p, pl, kv_dtype, out, out_dtype, lse, ws, true,
+  for (long g = 0, G = row_group_count(P, H); g < G; ++g) {
+    mla_impl::DecodeParams p;
+    Plan pl;
+    setup_decode(q, kv_cache, kv_dtype, kv_scale, block_table, max_blocks_per_seq, block_size,
+                 seq_lens, kv_begin, kv_end, B, P, H, row_group(P, H, g), max_kv_len,
+                 softmax_scale, num_splits, &p, &pl);
+    st = launch_verify(p, pl, kv_dtype, out, out_dtype, lse, ws, true,
                        static_cast<hipStream_t>(stream));
+    if (st != MLA_OK) return st;
+  }
+  return MLA_OK;
 }
 
 mla_status mla_merge_lse(const float* part_out, const float* part_lse, int S, int N, void* out,
@@ -385,7 +454,7 @@ mla_status mla_prefill(const void* q, const void* kv, int kv_dtype, float kv_sca
   if (B < 0 || T < 0 || max_seqlen < 0 || H < 1) return MLA_E_INVAL;
   if (kv_dtype != MLA_DTYPE_BF16 && kv_dtype != MLA_DTYPE_FP8_E4M3) return MLA_E_UNSUPPORTED;
   if (check_dtype_out(out_dtype) != MLA_OK) return MLA_E_UNSUPPORTED;
-  if (H > MLA_MAX_ROWS) return MLA_E_UNSUPPORTED;
+  if ((long)T * H > 0x7fffffffL) return MLA_E_UNSUPPORTED;
   if (!std::isfinite(softmax_scale)) return MLA_E_INVAL;
   if (kv_dtype == MLA_DTYPE_FP8_E4M3 && !finite_positive(kv_scale)) return MLA_E_INVAL;
   if (B == 0 || T == 0) return MLA_OK;

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     for (int row = 0; row < 16; ++row) {
       const int rr = rb * 16 + row;
       if (rr >= p.R) break;
-      const size_t n = (size_t)b * p.R + rr;
+      const size_t n = io_row(p, b, rr);
       for (int d = 0; d < kDV; d += 4) store_row4(p, n, d, (f32x4){0.f, 0.f, 0.f, 0.f});
       if (p.lse) p.lse[n] = -INFINITY;
     }
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     bf16x8 qreg[kKSteps];
     {
       const int rq = rb * 16 + col;
-      const uint16_t* qrow = p.q + ((size_t)b * p.R + min(rq, p.R - 1)) * kDK;
+      const uint16_t* qrow = p.q + io_row(p, b, min(rq, p.R - 1)) * kDK;
   #pragma unroll
       for (int kk = 0; kk < kKSteps; ++kk) {
         const bf16x8 v = *(const bf16x8*)(qrow + kdim(kk, grp));
@@ -470,7 +470,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     }
     const float inv = (Lb > 0.f) ? p.out_scale / Lb : 0.f;
     const float lse_v = (Lr > 0.f) ? (Mr + fast_log2(Lr)) * kLn2 : -INFINITY;
-    const size_t n = (size_t)b * p.R + rr;
+    const size_t n = io_row(p, b, rr);
     // the four waves' scaled rows summed: dims d .. d + 3 of output row orow_i
     auto merged = [&](int d) {
       f32x4 x = *(const f32x4*)(sm.red.o[0] + orow_i * kORow + d);
@@ -541,9 +541,10 @@ __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p)
   __shared__ float red[8][kDims + 4];
   __shared__ float gm[8], gl[8];
   const int tid = threadIdx.x;
-  const size_t n = blockIdx.x / kQ;
+  const size_t bn = blockIdx.x / kQ;  // row rr of sequence b of this launch's rows
   const int d0 = (int)(blockIdx.x % kQ) * kDims;
-  const int b = (int)(n / p.R), rr = (int)(n % p.R);
+  const int b = (int)(bn / p.R), rr = (int)(bn % p.R);
+  const size_t n = io_row(p, b, rr);
   const int w_first = p.seq_pieces[2 * b], w_last = p.seq_pieces[2 * b + 1];
   if (w_first == w_last) return;  // one piece held the whole sequence and wrote it
   const size_t R = p.R;

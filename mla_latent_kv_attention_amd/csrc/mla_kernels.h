@@ -13,7 +13,7 @@ namespace mla_impl {
 // segments of its piece, and the last piece to finish a sequence merges that
 // sequence's partials.
 struct DecodeParams {
-  const uint16_t* q;           // [B, R, 576] bf16, R = P * H
+  const uint16_t* q;           // [B, r_stride, 576] bf16; this launch's rows: R = P * H
   const uint8_t* kv;           // [num_blocks, block_size, 576] bf16 or fp8 codes
   const int32_t* block_table;  // [B, max_blocks]
   const int32_t* seq_lens;     // [B]
@@ -22,6 +22,11 @@ struct DecodeParams {
   int max_blocks;
   int block_size;              // multiple of 16
   int B, P, H, R, RB;          // RB = ceil(R / 16)
+  // A sequence of more than 64 query rows runs as several launches, each over a group of
+  // at most 64 of its rows (whole positions, or 64-head slices of one position):
+  int r_stride;                // rows per sequence in q, out and lse (the call's P * H)
+  int r_off;                   // this launch's first row within each sequence's rows
+  int len_shift;               // its last position is this many before the sequence's last
   int W;                       // pieces of the concatenated step list
   int seg_steps;               // virtual steps charged per sequence a piece touches
   float score_scale_log2;      // softmax_scale * kv_scale * log2(e)
@@ -32,9 +37,9 @@ struct DecodeParams {
   int* flags;                  // error flags (MLA_FLAG_*), ORed in; null: not reported
   int merge_in_kernel;         // 1: the last piece of a sequence merges; 0: launch_merge_shares
   int* seq_pieces;             // [B, 2]: first and last piece of each sequence (merge_in_kernel 0)
-  void* out;                   // [B * R, 512] fp32 or bf16
+  void* out;                   // [B * r_stride, 512] fp32 or bf16
   int out_bf16;
-  float* lse;                  // [B * R] or null
+  float* lse;                  // [B * r_stride] or null
 };
 
 // The same for sequences of 2 to 4 row blocks: one work-group per piece serves them all

@@ -40,9 +40,17 @@ struct SeqRange {
   int L, lo, hi, base, n;
 };
 
+// Row rr of sequence b in q, out and lse (this launch's rows sit at r_off in each sequence).
+__device__ __forceinline__ size_t io_row(const DecodeParams& p, int b, int rr) {
+  return (size_t)b * p.r_stride + p.r_off + rr;
+}
+
+// The sequence length as this launch sees it: a group of positions that ends
+// len_shift positions before the sequence's last keeps the same causal limits
+// (position j sees keys < L - P + j + 1) with L and P taken as the group's.
 __device__ __forceinline__ SeqRange seq_range(const DecodeParams& p, int b) {
   SeqRange r;
-  r.L = ((const kconst_i32*)p.seq_lens)[b];
+  r.L = ((const kconst_i32*)p.seq_lens)[b] - p.len_shift;
   r.lo = p.kv_begin ? max(((const kconst_i32*)p.kv_begin)[b], 0) : 0;
   r.hi = p.kv_end ? min(((const kconst_i32*)p.kv_end)[b], r.L) : r.L;
   r.base = r.lo & ~(kStep - 1);
@@ -129,7 +137,7 @@ __device__ __forceinline__ void raise_flag(const DecodeParams& p, int bit) {
 // Piece 0's check of sequence b's lengths against the stated contract (P <= seq_lens <=
 // max_blocks * block_size, kv_begin >= 0); results are undefined outside it.
 __device__ __forceinline__ void check_lengths(const DecodeParams& p, int b) {
-  const int L = p.seq_lens[b];
+  const int L = p.seq_lens[b] - p.len_shift;
   const bool bad = L < p.P || (long)L > (long)p.max_blocks * p.block_size ||
                    (p.kv_begin && p.kv_begin[b] < 0);
   if (bad) raise_flag(p, kFlagBadLengths);

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       p.seq_pieces[2 * b + 1] = 0;
     }
     for (int rr = 0; rr < p.R; ++rr) {
-      const size_t n = (size_t)b * p.R + rr;
+      const size_t n = io_row(p, b, rr);
       for (int d = 0; d < kDV; d += 4) store_row4(p, n, d, (f32x4){0.f, 0.f, 0.f, 0.f});
       if (p.lse) p.lse[n] = -INFINITY;
     }
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
     bf16x8 qreg[kKSteps];
     auto load_q = [&]() {
       if (scorer) {
-        const uint16_t* qrow = p.q + ((size_t)b * p.R + min(r, p.R - 1)) * kDK;
+        const uint16_t* qrow = p.q + io_row(p, b, min(r, p.R - 1)) * kDK;
 #pragma unroll
         for (int kk = 0; kk < kKSteps; ++kk) {
           const bf16x8 v = *(const bf16x8*)(qrow + kdim(kk, grp));
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       const float m = rowstat[rb][0][col], l = rowstat[rb][1][col], lb = rowstat[rb][2][col];
       const float inv = (lb > 0.f) ? p.out_scale / lb : 0.f;
       const float lse_v = (l > 0.f) ? (m + fast_log2(l)) * kLn2 : -INFINITY;
-      const size_t n = (size_t)b * p.R + rr;
+      const size_t n = io_row(p, b, rr);
       if (whole) {
 #pragma unroll
         for (int mt = 0; mt < kDvWave / 16; ++mt)
@@ -530,8 +530,8 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
     }
     __syncthreads();
     if (!last_flag) continue;
-    for (int rr = tid >> 4; rr < p.R; rr += 16) merge_pieces(p, b, rr, (size_t)b * p.R + rr,
-                                                             w_first, w_last);
+    for (int rr = tid >> 4; rr < p.R; rr += 16)
+      merge_pieces(p, b, rr, io_row(p, b, rr), w_first, w_last);
   }
 }
 

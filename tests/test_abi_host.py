@@ -70,7 +70,7 @@ def verify_args(**over):
     (dict(B=-1), -1),
     (dict(splits=-2), -1),
     (dict(max_kv_len=-5), -1),
-    (dict(P=5, H=16), -2),          # 80 query rows per sequence: more than one work-group holds
+    (dict(P=257, H=256), -2),       # more query rows per sequence than MLA_MAX_CALL_ROWS
     (dict(kv_dtype=7), -2),
     (dict(out_dtype=1), -2),        # FP8 is a cache format, not an output format
     (dict(block_size=24), -1),
@@ -90,7 +90,7 @@ def test_verify_rejects_bad_arguments_before_launch(lib, over, status):
 
 
 @pytest.mark.parametrize("over,status", [
-    (dict(P=0), -1), (dict(H=0), -1), (dict(B=-1), -1), (dict(P=5, H=16), -2),
+    (dict(P=0), -1), (dict(H=0), -1), (dict(B=-1), -1), (dict(P=257, H=256), -2),
     (dict(kv_dtype=7), -2), (dict(out_dtype=1), -2), (dict(block_size=24), -1),
     (dict(kv_dtype=1, kv_scale=0.0), -1), (dict(out=None), -1),
 ])
@@ -154,7 +154,7 @@ def test_top_k_renorm_rejects_bad_arguments_and_sizes_its_workspace(lib):
 def test_prefill_rejects_bad_arguments(lib):
     P = ctypes.c_void_p(0x1000)
     assert lib.mla_prefill(P, P, 0, 1.0, P, 1, 16, 16, 0, 0.07, P, 0, None, None) == -1
-    assert lib.mla_prefill(P, P, 0, 1.0, P, 1, 16, 16, 65, 0.07, P, 0, None, None) == -2
+    assert lib.mla_prefill(P, P, 0, 1.0, P, 1, 16, 16, 1 << 28, 0.07, P, 0, None, None) == -2
     assert lib.mla_prefill(P, P, 3, 1.0, P, 1, 16, 16, 12, 0.07, P, 0, None, None) == -2
     assert lib.mla_prefill(P, P, 1, -1.0, P, 1, 16, 16, 12, 0.07, P, 0, None, None) == -1
     assert lib.mla_prefill(None, P, 0, 1.0, P, 1, 16, 16, 12, 0.07, P, 0, None, None) == -1
@@ -226,7 +226,25 @@ def test_counter_capacity_is_enforced(lib):
 def test_explicit_split_count_is_honoured(lib):
     assert lib.mla_decode_num_splits(2, 1, 12, 1000, 7, 256) == 7
     assert lib.mla_decode_num_splits(2, 1, 12, 10, 3, 256) == 3
-    assert lib.mla_decode_num_splits(2, 5, 16, 10, 3, 256) == -2
+    assert lib.mla_decode_num_splits(2, 5, 16, 10, 3, 256) == 3  # each row group's plan
+    assert lib.mla_decode_num_splits(2, 257, 256, 10, 3, 256) == -2
+
+
+@pytest.mark.parametrize("B,P,H,L,S,groups", [
+    (2, 5, 16, 1000, 0, [(4, 16), (1, 16)]),     # whole positions: 4 per group
+    (3, 1, 128, 5000, 0, [(1, 64)]),             # 64-head slices of one position
+    (1, 3, 100, 40000, 0, [(1, 64), (1, 36)]),   # slices of 64 and 36 heads, per position
+    (4, 9, 8, 20000, 12, [(8, 8), (1, 8)]),
+    (2, 65, 1, 300, 0, [(64, 1), (1, 1)])])
+def test_row_groups_share_one_workspace(lib, B, P, H, L, S, groups):
+    """More than 64 query rows per sequence run as groups of at most 64 rows, one launch
+    each over the same workspace: the call needs what its largest group shape needs,
+    and its piece count is the first group's."""
+    want = max(lib.mla_decode_workspace_size(B, gp, gh, L, S) for gp, gh in groups)
+    assert lib.mla_decode_workspace_size(B, P, H, L, S) == want
+    gp, gh = groups[0]
+    assert lib.mla_decode_num_splits(B, P, H, L, S, 256) == \
+        lib.mla_decode_num_splits(B, gp, gh, L, S, 256)
 
 
 def test_read_probe_rejects_bad_arguments_before_launch():
