@@ -510,6 +510,83 @@ def run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check
     result["prefill"] = res
 
 
+TIMELINE_PHASES = {
+    "decode": ["work-group starts", "step-list scan done", "streaming loop ends",
+               "wave merge done", "result written / share published", "last piece's merge done"],
+    "verify": ["work-group starts", "step-list scan done", "queries and tile 0 in",
+               "first tile-loop barrier", "tile loop ends", "normalisers shared",
+               "result written / share published"],
+}
+
+
+def run_timeline(args, torch, mi, mla, bf16_tensor, cache_to_device, dev):
+    """Per-work-group phase stamps (libmla_timeline.so: the attention library with stamps of
+    the 100 MHz real-time counter compiled in): for each workload, `samples` calls each
+    following another call on the stream, the stamps of the later one read; per phase the
+    median / p90 / max over work-groups of the time from the call's first work-group start,
+    averaged over the samples.  Stamps a call did not write (its own phase was not reached,
+    e.g. a merge by another piece) are older than its start and left out."""
+    import ctypes
+    lib = mla.library()
+    for fn in ("mla_timeline_read_decode", "mla_timeline_read_verify"):
+        getattr(lib, fn).argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+        getattr(lib, fn).restype = ctypes.c_int
+    groups, slots = 4096, 8
+    res = {}
+    for name, kind in ((DECODE_WORKLOAD, "decode"), ("verify_b4_p4_h12_l32768_bf16", "verify")):
+        w = mi.WORKLOADS[name]
+        log("timeline:", name)
+        d = mi.decode_inputs(w)
+        q_np, cache = d["q"], d["cache"]
+        B, P, H = q_np.shape[:3]
+        L = [int(x) for x in cache.seq_lens]
+        kv0, bt, sl = cache_to_device(cache, dev)
+        pools = [kv0] + [kv0.clone() for _ in range(2)]
+        q = bf16_tensor(q_np, dev).reshape(B, P, H, 576)
+        out = torch.empty((B, P, H, 512), dtype=torch.float32, device=dev)
+        lse = torch.empty((B, P, H), dtype=torch.float32, device=dev)
+        ws = torch.zeros(max(1, mla.decode_workspace_size(B, P, H, max(L))), dtype=torch.uint8,
+                         device=dev)
+        fns = [mla.verify_launcher(q, kv, bt, sl, softmax_scale=w.softmax_scale,
+                                   kv_scale=cache.kv_scale, max_kv_len=max(L), out=out, lse=lse,
+                                   workspace=ws) for kv in pools]
+        G = mla.decode_num_splits(B, P, H, max(L))
+        if kind == "decode":
+            G *= (P * H + 15) // 16  # one work-group per (piece, row block)
+        read = getattr(lib, "mla_timeline_read_" + kind)
+        buf = np.zeros(groups * slots, np.uint64)
+        for i in range(10):
+            fns[i % 3]()
+        per = []
+        for sample in range(args.timeline_samples):
+            fns[sample % 3]()
+            if read(buf.ctypes.data, buf.nbytes) != 0:  # read and clear
+                raise RuntimeError("timeline stamps could not be read")
+            fns[(sample + 1) % 3]()
+            fns[(sample + 2) % 3]()
+            if read(buf.ctypes.data, buf.nbytes) != 0:
+                raise RuntimeError("timeline stamps could not be read")
+            t = buf.reshape(groups, slots)[:G].astype(np.float64)
+            t0 = t[:, 0].min()  # the later call's start: every work-group stamps slot 0
+            rows = []
+            for k in range(len(TIMELINE_PHASES[kind])):
+                v = t[:, k]
+                v = (v[v >= t0] - t0) / 100.0  # 100 MHz ticks -> us
+                rows.append((np.median(v), np.percentile(v, 90), v.max()) if len(v) else
+                            (float("nan"),) * 3)
+            per.append(rows)
+        a = np.array(per)  # samples x phases x 3
+        tab = {ph: [round(float(x), 2) for x in np.nanmean(a[:, k, :], axis=0)]
+               for k, ph in enumerate(TIMELINE_PHASES[kind])}
+        res[name] = {"work_groups": G, "us_median_p90_max": tab,
+                     "samples": args.timeline_samples}
+        log("%s (%d work-groups; us from the first work-group's start: median / p90 / max)"
+            % (name, G))
+        for ph, v in tab.items():
+            log("  %-36s %8.2f %8.2f %8.2f" % (ph, v[0], v[1], v[2]))
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -526,6 +603,10 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=5)
     ap.add_argument("--secondary", default="",
                     help="comma-separated secondary workloads to run (default: all)")
+    ap.add_argument("--timeline", action="store_true",
+                    help="only print per-work-group phase timelines of the headline decode and "
+                         "the 4 x 4 x 32K verify (loads libmla_timeline.so) and exit")
+    ap.add_argument("--timeline-samples", type=int, default=8)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (the reference kernel "
                          "for scaling HBM byte counters) and exit")
@@ -552,6 +633,14 @@ def main():
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     from parity import bf16_tensor, cache_to_device, check_lse, check_out
 
+    if args.timeline:
+        mla.LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(mla.__file__)),
+                                    "libmla_timeline.so")
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        res = run_timeline(args, torch, mi, mla, bf16_tensor, cache_to_device, dev)
+        print(json.dumps({"timeline": res}), flush=True)
+        return
     mla.library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -1,6 +1,8 @@
 """Build the HIP libraries for gfx950 with hipcc (in-tree): libmla.so, the attention
-library behind include/mla.h, and libmla_read_probe.so, the benchmark's plain-read
-probe (a measurement helper kept out of the attention library)."""
+library behind include/mla.h; libmla_read_probe.so, the benchmark's plain-read probe
+(a measurement helper kept out of the attention library); and libmla_timeline.so, the
+attention library again with per-work-group phase stamps compiled in (MLA_TIMELINE),
+which only `bench.py --timeline` loads."""
 from __future__ import annotations
 
 import os
@@ -15,6 +17,7 @@ SOURCES = ["mla_api.cpp", "mla_decode.hip", "mla_verify.hip", "mla_prefill.hip",
            "mla_sampling.hip"]
 PROBE_LIB = os.path.join(PKG, "libmla_read_probe.so")
 PROBE_SOURCES = [os.path.join("probe", "mla_read_probe.hip")]
+TIMELINE_LIB = os.path.join(PKG, "libmla_timeline.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -26,13 +29,14 @@ FLAGS = [
 ]
 
 
-def _build_one(sources, lib, verbose: bool) -> str:
+def _build_one(sources, lib, verbose: bool, defines=()) -> str:
     srcs = []
     for s in sources:
         path = os.path.join(CSRC, s)
         srcs += (["-x", "hip"] if s.endswith(".cpp") else []) + [path]
     tmp = lib + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + ["-I", os.path.join(CSRC, "probe")] + srcs + ["-o", tmp]
+    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + ["-I", os.path.join(CSRC, "probe")] + \
+        srcs + ["-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -47,8 +51,9 @@ def _build_one(sources, lib, verbose: bool) -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile both libraries; returns the attention library's path."""
+    """Compile the three libraries; returns the attention library's path."""
     _build_one(PROBE_SOURCES, PROBE_LIB, verbose)
+    _build_one(SOURCES, TIMELINE_LIB, verbose, defines=("MLA_TIMELINE",))
     return _build_one(SOURCES, LIB, verbose)
 
 

@@ -50,6 +50,12 @@
 namespace mla_impl {
 using namespace mla_dev;
 
+#ifdef MLA_TIMELINE
+// per work-group: start, step-list scan done, then for its last segment: streaming loop
+// end, wave merge done, result written or share published (counter bumped), merge done
+__device__ unsigned long long decode_stamps[kStampGroups * kStampSlots];
+#endif
+
 namespace {
 
 constexpr int kWaves = 4;
@@ -92,6 +98,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
   const int per = 8 * p.RB;
   const int full = (W / 8) * per;
   const int id = blockIdx.x;
+  MLA_STAMP(decode_stamps, 0);
   const int rb = id < full ? (id % per) / 8 : (id - full) % p.RB;
   const int w = id < full ? (id / per) * 8 + id % 8 : 8 * (W / 8) + (id - full) / p.RB;
   if (w >= W) return;
@@ -208,6 +215,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
   }
   const int b_first = (int)seg[0];
   long o = (long)seg[1];  // list offset of sequence b
+  MLA_STAMP(decode_stamps, 1);
 
   for (int b = b_first; b < p.B && o < S1; ++b) {
     // the first sequence's range came with the scan; later ones are read here
@@ -429,6 +437,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     m_ref = (m_max > m_ref + kCap) ? m_max : m_ref;
     }
 
+    MLA_STAMP(decode_stamps, 2);
     // ---- merge the four waves: one round through LDS ----
     const float l_row = wave_sum16x4(l_run);
     const float lb_row = wave_sum16x4(lb_run);
@@ -451,6 +460,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     }
     __syncthreads();
 
+    MLA_STAMP(decode_stamps, 3);
     // ---- this piece's result for sequence b: final rows, or a partial + merge ----
     const int orow_i = tid >> 4;  // 16 threads per output row
     const int rr = rb * 16 + orow_i;
@@ -487,6 +497,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
         }
         if (p.lse && (tid & 15) == 0) p.lse[n] = lse_v;
       }
+      MLA_STAMP(decode_stamps, 4);
       continue;
     }
     const size_t slot = (size_t)(w + b) * p.R;  // slot w + b is unique per (piece, sequence)
@@ -501,7 +512,10 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
         }
       }
     }
-    if (!p.merge_in_kernel) continue;  // a separate launch merges the shares
+    if (!p.merge_in_kernel) {  // a separate launch merges the shares
+      MLA_STAMP(decode_stamps, 4);
+      continue;
+    }
     // Publish the partial; the last piece to finish sequence b merges all of them.
     // Every thread waits for its agent-coherent stores to be acknowledged before
     // the barrier, so they are visible device-wide before the counter moves; the
@@ -518,8 +532,13 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
       last_flag = last;
     }
     __syncthreads();
+    MLA_STAMP(decode_stamps, 4);
     if (!last_flag) continue;
     if (rr_ok) merge_pieces(p, b, rr, n, w_first, w_last);
+#ifdef MLA_TIMELINE
+    __syncthreads();
+    MLA_STAMP(decode_stamps, 5);
+#endif
   }
 }
 
@@ -684,6 +703,19 @@ __global__ __launch_bounds__(256) void clear_i32_kernel(int* p, long n) {
 }  // namespace
 
 int decode_grid_size(int W, int RB) { return W * RB; }
+
+#ifdef MLA_TIMELINE
+// Copies the stamps of the launches since the last read to host memory, then zeroes them.
+extern "C" int mla_timeline_read_decode(void* host, size_t bytes) {
+  void* dev = nullptr;
+  if (bytes > sizeof(decode_stamps) || hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpyFromSymbol(host, HIP_SYMBOL(decode_stamps), bytes) != hipSuccess ||
+      hipGetSymbolAddress(&dev, HIP_SYMBOL(decode_stamps)) != hipSuccess ||
+      hipMemset(dev, 0, sizeof(decode_stamps)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return -1;
+  return 0;
+}
+#endif
 
 hipError_t launch_clear_i32(int* p, long n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;

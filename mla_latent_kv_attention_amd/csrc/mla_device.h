@@ -222,4 +222,25 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
+// Phase stamps of the timeline build (libmla_timeline.so, compiled with MLA_TIMELINE):
+// the first thread of work-group g writes the 100 MHz real-time counter at phase
+// boundary s to buf[g * kStampSlots + s], for the first kStampGroups work-groups.  The
+// stores are thread 0's only and come after (never between) the copies whose waits
+// count outstanding operations, so they can only make those waits stricter.  Every
+// other build compiles the stamps out.
+constexpr int kStampGroups = 4096;
+constexpr int kStampSlots = 8;
+
 }  // namespace mla_dev
+
+#ifdef MLA_TIMELINE
+#define MLA_STAMP(buf, s)                                                           \
+  do {                                                                              \
+    if (threadIdx.x == 0 && blockIdx.x < mla_dev::kStampGroups)                     \
+      (buf)[blockIdx.x * mla_dev::kStampSlots + (s)] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define MLA_STAMP(buf, s) \
+  do {                    \
+  } while (0)
+#endif

@@ -34,6 +34,13 @@
 namespace mla_impl {
 using namespace mla_dev;
 
+#ifdef MLA_TIMELINE
+// per work-group: start, step-list scan done, then for its last segment: queries and
+// tile 0 in, first barrier of the tile loop, tile loop end, row normalisers shared,
+// result written or share published
+__device__ unsigned long long verify_stamps[kStampGroups * kStampSlots];
+#endif
+
 namespace {
 
 constexpr int kWaves = 4;
@@ -80,6 +87,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
   const int grp = lane >> 4;  // k-group (A, B) / 4-row group (C)
   const int W = p.W;
   const int w = blockIdx.x;
+  MLA_STAMP(verify_stamps, 0);
   if (w >= W) return;
   const size_t row_bytes = kFp8 ? kDK : 2 * kDK;
 
@@ -182,6 +190,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
   }
   const int b_first = (int)seg[0];
   long o = (long)seg[1];
+  MLA_STAMP(verify_stamps, 1);
 
   for (int b = b_first; b < p.B && o < S1; ++b) {
     SeqRange sr;
@@ -404,6 +413,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
     if constexpr (!kFp8) issue_tile(0);
     load_q();
     wait_vmcnt<0>();
+    MLA_STAMP(verify_stamps, 2);
     for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
       for (int rb = 0; rb < kRB; ++rb)
@@ -435,6 +445,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
           wait_vmcnt<0>();
       }
       __syncthreads();
+      if (pass == 0) MLA_STAMP(verify_stamps, 3);
       if (scorer) score_tile(0);
       for (int k = 0; k < n_tiles; ++k) {
         if constexpr (kFp8) {
@@ -459,6 +470,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
         if (scorer && k + 1 < n_tiles) score_tile(k + 1);
         value_tile(k);
       }
+      MLA_STAMP(verify_stamps, 4);
       // a row beyond its cap: the work-group runs the segment again, those rows from
       // their true maximum (the others recompute bit-identically)
       if (tid == 0) rerun = 0;
@@ -469,6 +481,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       m_ref = (m_max > m_ref + kCap) ? m_max : m_ref;
     }
 
+    MLA_STAMP(verify_stamps, 5);
     // ---- normalisers: the owners publish each row's, every wave scales its dims ----
     if (scorer) {
       const float l_row = wave_sum16x4(l_run), lb_row = wave_sum16x4(lb_run);  // whole wave
@@ -514,6 +527,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
         }
       }
     }
+    MLA_STAMP(verify_stamps, 6);
     if (whole) continue;
     if (!p.merge_in_kernel) continue;  // a separate launch merges the shares
     // publish, then the last piece of the sequence merges every share (as in the decode
@@ -536,6 +550,19 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
 }
 
 }  // namespace
+
+#ifdef MLA_TIMELINE
+// Copies the stamps of the launches since the last read to host memory, then zeroes them.
+extern "C" int mla_timeline_read_verify(void* host, size_t bytes) {
+  void* dev = nullptr;
+  if (bytes > sizeof(verify_stamps) || hipDeviceSynchronize() != hipSuccess ||
+      hipMemcpyFromSymbol(host, HIP_SYMBOL(verify_stamps), bytes) != hipSuccess ||
+      hipGetSymbolAddress(&dev, HIP_SYMBOL(verify_stamps)) != hipSuccess ||
+      hipMemset(dev, 0, sizeof(verify_stamps)) != hipSuccess || hipDeviceSynchronize() != hipSuccess)
+    return -1;
+  return 0;
+}
+#endif
 
 hipError_t launch_verify_shared(const DecodeParams& p, bool kv_fp8, hipStream_t stream) {
   if (p.W <= 0) return hipSuccess;

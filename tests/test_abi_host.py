@@ -268,3 +268,19 @@ def test_read_probe_rejects_bad_arguments_before_launch():
 
 def test_attention_library_does_not_export_the_probe(lib):
     assert not hasattr(lib, "mla_hbm_read_probe")
+
+
+def test_phase_stamps_only_in_the_timeline_library(lib):
+    """The attention library has the stamps compiled out; libmla_timeline.so (the same
+    sources built with MLA_TIMELINE, loaded only by `bench.py --timeline`) exports their
+    readers and every entry point of the attention library."""
+    import mla_latent_kv_attention_amd as m
+    for fn in ("mla_timeline_read_decode", "mla_timeline_read_verify"):
+        assert not hasattr(lib, fn)
+    path = os.path.join(os.path.dirname(m.LIB_PATH), "libmla_timeline.so")
+    if not os.path.exists(path):
+        pytest.skip("libmla_timeline.so is not built")
+    tl = ctypes.CDLL(path)
+    for fn in ("mla_timeline_read_decode", "mla_timeline_read_verify", "mla_verify",
+               "mla_verify_noalloc", "mla_prefill", "mla_decode_workspace_size"):
+        assert hasattr(tl, fn), fn
