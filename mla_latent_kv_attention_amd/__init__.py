@@ -169,6 +169,7 @@ def decode_workspace_size(B: int, P: int, H: int, max_kv_len: int, num_splits: i
 WORKSPACE_FLAGS_OFFSET = 4 * 65536
 FLAG_STALE_COUNTERS = 1
 FLAG_BAD_LENGTHS = 2
+FLAG_BAD_BLOCKS = 4
 
 
 class WorkspaceError(RuntimeError):
@@ -181,6 +182,8 @@ class WorkspaceError(RuntimeError):
                         "complete, or calls overlapped on this workspace)")
         if flags & FLAG_BAD_LENGTHS:
             what.append("a sequence length or kv_begin outside the contract")
+        if flags & FLAG_BAD_BLOCKS:
+            what.append("a negative block-table entry (block 0 was read in its place)")
         super().__init__("decode workspace flags 0x%x: %s" % (flags, "; ".join(what) or "?"))
         self.flags = flags
 

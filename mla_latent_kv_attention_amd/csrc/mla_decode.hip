@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     const kconst_i32* bt = (const kconst_i32*)(p.block_table + (size_t)b * p.max_blocks);
     auto step_row = [&](int t0) -> long {
       t0 = __builtin_amdgcn_readfirstlane(t0);
-      return (long)bt[t0 / p.block_size] * p.block_size + t0 % p.block_size;
+      return block_id(p, bt, t0 / p.block_size) * p.block_size + t0 % p.block_size;
     };
     auto load_step = [&](long row0, int t0, u32x4* dst) {
       // all 16 tokens of an aligned step sit in one block; clamping into the visible

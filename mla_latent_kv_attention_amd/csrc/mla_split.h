@@ -129,6 +129,7 @@ __device__ __forceinline__ void merge_pieces(const DecodeParams& p, int b, int r
 // Error flags (MLA_FLAG_* in mla.h): bits ORed into the workspace's flags word.
 constexpr int kFlagStaleCounters = 1;
 constexpr int kFlagBadLengths = 2;
+constexpr int kFlagBadBlocks = 4;
 
 __device__ __forceinline__ void raise_flag(const DecodeParams& p, int bit) {
   if (p.flags) __hip_atomic_fetch_or(p.flags, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -141,6 +142,19 @@ __device__ __forceinline__ void check_lengths(const DecodeParams& p, int b) {
   const bool bad = L < p.P || (long)L > (long)p.max_blocks * p.block_size ||
                    (p.kv_begin && p.kv_begin[b] < 0);
   if (bad) raise_flag(p, kFlagBadLengths);
+}
+
+// Physical block of logical block i in a sequence's block-table row bt (a uniform
+// index: the id comes through the scalar cache).  A negative id, outside the
+// contract, would address memory before the cache: block 0 is read instead and the
+// call is flagged.
+__device__ __forceinline__ long block_id(const DecodeParams& p, const kconst_i32* bt, int i) {
+  const int id = bt[i];
+  if (id < 0) {
+    raise_flag(p, kFlagBadBlocks);
+    return 0;
+  }
+  return id;
 }
 
 // Sum over the work-group (256 threads); sh holds 4 values and is free on entry.

@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       const int hb = th < hi_all ? th : ((hi_all - 1) & ~(kStep - 1));
       Half h;
       h.hb = hb;
-      h.row0 = (long)bt[hb / p.block_size] * p.block_size + hb % p.block_size;
+      h.row0 = block_id(p, bt, hb / p.block_size) * p.block_size + hb % p.block_size;
       return h;
     };
     // byte address of token t's 16-byte chunk pc, for a token of half h

@@ -125,3 +125,37 @@ def test_in_launch_merge_soak(mla):
         mla.check_decode_workspace(case[7])
     print("soak: %d calls bitwise equal" % calls, flush=True)
     assert calls >= 2000
+
+
+@pytest.mark.parametrize("hint", [2000, 65536])  # the one-row-block-per-work-group and shared kernels
+def test_negative_block_ids_are_flagged_and_read_as_block_zero(mla, hint):
+    """A negative block-table entry (outside the contract) for a visible block of sequence 1:
+    the kernels read block 0 in its place (never memory before the cache) and flag the call;
+    the other sequences are checked against the oracle as usual.  The allocation-free entry
+    point (no flags) reads block 0 the same way."""
+    lens = [300, 700, 900]
+    cache = mi.paged_cache(7304, lens, 64, "fp8")
+    q_np = mi.normal_bf16_bits(7304, 3, (3, 4, 12, 576))
+    kv, bt, sl = cache_to_device(cache, DEV)
+    bt[1, 2] = -3  # tokens 128 .. 191 of sequence 1
+    q = bf16_tensor(q_np, DEV)
+    ws = torch.zeros(mla.decode_workspace_size(3, 4, 12, hint, 9), dtype=torch.uint8, device=DEV)
+    o, l = mla.verify(q, kv, bt, sl, softmax_scale=SIGMA, kv_scale=cache.kv_scale,
+                      max_kv_len=hint, num_splits=9, workspace=ws)
+    torch.cuda.synchronize()
+    assert mla.decode_workspace_flags(ws) == mla.FLAG_BAD_BLOCKS
+    with pytest.raises(mla.WorkspaceError):
+        mla.check_decode_workspace(ws)
+    ref_o, ref_l = oracle.decode(q_np, cache.kv, True, cache.kv_scale, cache.block_table,
+                                 cache.seq_lens, SIGMA)
+    for b in (0, 2):
+        check_out(o[b], ref_o[b])
+        check_lse(l[b], ref_l[b])
+    o2 = torch.full_like(o, float("nan"))
+    l2 = torch.full_like(l, float("nan"))
+    mla.verify_noalloc(q, kv, bt, sl, softmax_scale=SIGMA, kv_scale=cache.kv_scale,
+                       max_kv_len=hint, num_splits=9, out=o2, lse=l2)
+    torch.cuda.synchronize()
+    for b in (0, 2):
+        check_out(o2[b], ref_o[b])
+        check_lse(l2[b], ref_l[b])
