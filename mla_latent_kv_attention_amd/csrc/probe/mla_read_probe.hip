@@ -13,7 +13,10 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Work-group g reads words [g * per_wg, min((g + 1) * per_wg, n16)); eight 16-byte
-// loads per thread are in flight per iteration.  The xor keeps the loads alive.
+// loads per thread are in flight per iteration, each wave-wide load a contiguous 1 KB,
+// with the nontemporal hint (the fastest plain read measured on this chip: about
+// 6.6 TB/s at 512 work-groups against 5.6 - 5.8 TB/s without the hint).  The xor keeps
+// the loads alive.
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* __restrict__ src,
                                                          size_t n16, size_t per_wg,
                                                          uint32_t* __restrict__ sink) {
@@ -26,7 +29,7 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4_t* __restri
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const size_t j = i + 256 * (size_t)u;
-      v[u] = j < end ? src[j] : (u32x4_t){0u, 0u, 0u, 0u};
+      v[u] = j < end ? __builtin_nontemporal_load(src + j) : (u32x4_t){0u, 0u, 0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) acc ^= v[u];
