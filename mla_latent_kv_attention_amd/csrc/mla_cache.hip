@@ -14,6 +14,8 @@
 // of BF16, one 16-byte store of FP8 codes (or two of BF16).  Consecutive threads
 // take consecutive chunks, so a wave reads and writes contiguous runs.  The op is
 // HBM-bound: 1,152 bytes in and 576 (FP8) or 1,152 (BF16) bytes out per row.
+#include <cmath>
+
 #include "mla_device.h"
 #include "mla_kernels.h"
 
@@ -43,7 +45,25 @@ __device__ __forceinline__ uint32_t fp8_e4m3fn_code(float y) {
   return code | sign;
 }
 
-template <bool kFp8>
+// fp32(x / s), correctly rounded, from r = fp32(1 / s) and one fused correction: the
+// product y0 = x * r is within an ulp of x / s, the residual x - s * y0 is exact in an
+// fma, and y0 + r * residual rounded once is the correctly rounded quotient when
+// nothing underflows or overflows (Markstein's theorem on division by a correctly
+// rounded reciprocal).  The code only depends on the exact quotient between 2^-10 and
+// 448, so the correction is applied where |y0| >= 2^-100 and y0 is finite: below that
+// y0 carries x's sign and codes to a signed zero (where the correction could cancel to
+// +0), and an infinite y0 saturates like the infinite or huge x / s.  Three or four
+// instructions instead of a division.
+__device__ __forceinline__ float div_by_scale(float x, float s, float r) {
+  const float y0 = x * r;
+  const float e = __builtin_fmaf(-s, y0, x);
+  const bool correct = __builtin_fabsf(y0) >= 0x1p-100f && __builtin_isfinite(y0);
+  return correct ? __builtin_fmaf(e, r, y0) : y0;
+}
+
+// kFastDiv: the quotient through div_by_scale, for scales whose reciprocal is a normal
+// fp32 number (the host checks); otherwise a correctly rounded division per value.
+template <bool kFp8, bool kFastDiv>
 __global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t* __restrict__ latent,
                                                           long N, const int32_t* __restrict__ slot,
                                                           uint8_t* __restrict__ kv,
@@ -58,6 +78,7 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t* __rest
   const u32x4 lo = *(const u32x4*)src;
   const u32x4 hi = *(const u32x4*)(src + 8);
   if constexpr (kFp8) {
+    const float r = __fdiv_rn(1.f, kv_scale);
     const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     u32x4 out;
 #pragma unroll
@@ -68,8 +89,10 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t* __rest
         const uint32_t pair = w[2 * q + h];
         const float x0 = __uint_as_float(pair << 16);          // BF16 -> fp32, exact
         const float x1 = __uint_as_float(pair & 0xFFFF0000u);
-        word |= fp8_e4m3fn_code(__fdiv_rn(x0, kv_scale)) << (16 * h);
-        word |= fp8_e4m3fn_code(__fdiv_rn(x1, kv_scale)) << (16 * h + 8);
+        const float y0 = kFastDiv ? div_by_scale(x0, kv_scale, r) : __fdiv_rn(x0, kv_scale);
+        const float y1 = kFastDiv ? div_by_scale(x1, kv_scale, r) : __fdiv_rn(x1, kv_scale);
+        word |= fp8_e4m3fn_code(y0) << (16 * h);
+        word |= fp8_e4m3fn_code(y1) << (16 * h + 8);
       }
       out[q] = word;
     }
@@ -89,12 +112,17 @@ hipError_t launch_cache_write(const uint16_t* latent, long N, const int32_t* slo
   if (items == 0) return hipSuccess;
   const long blocks = (items + 255) / 256;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
-  if (kv_fp8)
-    hipLaunchKernelGGL(cache_write_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       latent, N, slot, (uint8_t*)kv, kv_scale, num_slots);
+  const float r = 1.f / kv_scale;  // IEEE division on the host: fp32(1 / kv_scale)
+  const bool fast = std::isnormal(r);
+  if (kv_fp8 && fast)
+    hipLaunchKernelGGL((cache_write_kernel<true, true>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, latent, N, slot, (uint8_t*)kv, kv_scale, num_slots);
+  else if (kv_fp8)
+    hipLaunchKernelGGL((cache_write_kernel<true, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, latent, N, slot, (uint8_t*)kv, kv_scale, num_slots);
   else
-    hipLaunchKernelGGL(cache_write_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream,
-                       latent, N, slot, (uint8_t*)kv, kv_scale, num_slots);
+    hipLaunchKernelGGL((cache_write_kernel<false, false>), dim3((unsigned)blocks), dim3(256), 0,
+                       stream, latent, N, slot, (uint8_t*)kv, kv_scale, num_slots);
   return hipGetLastError();
 }
 

@@ -114,3 +114,24 @@ def test_write_then_decode(mla):
                            cache.seq_lens, sigma)
     check_out(out, ro)
     check_lse(lse, rl)
+
+
+@pytest.mark.parametrize("scale", [5.0 / 448.0, 1.0, 3.7e-3, 0.0123, float(np.nextafter(np.float32(2), np.float32(0))),
+                                   float(np.float32(1) + np.float32(2.0 ** -23)), 2.0 ** -20, 3e-30, 7e29,
+                                   1e-39, 3e38])
+def test_every_bf16_value_codes_exactly(mla, scale):
+    """All 65,536 BF16 bit patterns (zeros, subnormals, every exponent, infinities, NaNs)
+    through the FP8 write at scales with awkward reciprocals: the kernel's quotient
+    (reciprocal, product and one fused correction) must code exactly as fp32(x / scale).
+    A scale whose reciprocal is not a normal number (1e-39, 3e38) takes the divisions."""
+    scale = float(np.float32(scale))
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    latent = np.resize(bits, ((bits.size + 575) // 576) * 576).reshape(-1, 576)
+    N = latent.shape[0]
+    slot = np.arange(N, dtype=np.int32)
+    kv = np.zeros((N, 576), np.uint8)
+    got = gpu_write(mla, latent, slot, kv, scale)
+    want = oracle.cache_write(latent, slot, kv, True, scale)
+    bad = np.argwhere(got != want)
+    assert bad.size == 0, "scale %r: %d codes differ, first at %s (x bits 0x%04x: gpu 0x%02x, oracle 0x%02x)" % (
+        scale, len(bad), bad[0].tolist(), latent[tuple(bad[0])], got[tuple(bad[0])], want[tuple(bad[0])])
