@@ -23,11 +23,14 @@
 // Each wave keeps its own online-softmax state and a 16-row x 512 fp32
 // accumulator, so no wave waits for another until the segment is done; each
 // wave holds the row block's 18 Q^T fragments in registers.  Per step:
-//   1. every lane loads 8 (bf16) or 16 (fp8) key values of one token straight
-//      from the paged cache into MFMA A-operand registers (16 B per load; fp8
-//      is widened to bf16 exactly); a ring of register buffers keeps the next
-//      steps in flight (three for fp8 caches, two for bf16), and block ids come
-//      through the scalar cache one step early;
+//   1. the step's 16 latent rows come in with 16-byte loads per lane, a ring of
+//      two register buffers keeping the next step in flight (block ids come
+//      through the scalar cache a step early).  BF16: each lane loads its
+//      MFMA A-operand fragments (8 key values of one token) straight from the
+//      cache.  FP8: the step's 9 KB are loaded as whole 1 KB spans with the
+//      nontemporal hint and written as they stand to a per-wave LDS stage, from
+//      which the lanes read their fragments back (16 codes of one token,
+//      widened to bf16 exactly);
 //   2. S^T[16 tokens x 16 rows] = K Q^T with 18 bf16 MFMA 16x16x32 (Q^T, the
 //      B operand, from registers);
 //   3. masking and the softmax numerator run on the 4 scores each lane holds,
@@ -35,12 +38,13 @@
 //      VALU lane swaps (v_permlane16/32_swap, no LDS round trip); each row's
 //      reference maximum is fixed at its first visible score, so the
 //      accumulator is never rescaled inside the loop (see the step loop);
-//   4. the value part (first 512 dims) of the same registers goes to a per-wave
-//      LDS tile, is read back transposed with ds_read_b64_tr_b16 and feeds
-//      O^T[512 x 16] += V^T P^T with 32 bf16 MFMA 16x16x16; P stays in
-//      registers because the score tile's layout is the B operand's layout.
-//      The two halves are software-pipelined: step i + 1's score half runs
-//      before step i's value half (two value tiles per wave).
+//   4. O^T[512 x 16] += V^T P^T, with P in registers as the score tile left it
+//      (its layout is the B operand's).  BF16: the value part (first 512 dims)
+//      of the fragments goes to a per-wave LDS tile and is read back transposed
+//      with ds_read_b64_tr_b16 for 32 MFMA 16x16x16; step i + 1's score half
+//      runs before step i's value half (two value tiles per wave).  FP8: two
+//      steps at a time, V^T read from the two stages with ds_read_b64_tr_b8 and
+//      widened, 32 MFMA 16x16x32 over the pair's 32 tokens.
 // At the end of a segment the four waves merge through LDS and the work-group
 // writes either the final rows (the piece holds the whole sequence) or its share.
 #include "mla_device.h"
@@ -63,10 +67,17 @@ constexpr int kKSteps = 18;     // 576 / 32
 constexpr int kVRow = 528;      // LDS row stride (bf16) of a wave's value tile (512 + 16 pad)
 constexpr int kORow = 516;      // LDS row stride (fp32) of the merged output tile
 constexpr float kCap = 64.0f;   // log2 units a score may exceed its row's reference max
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedValu = 0x2, kSchedMfma = 0x8, kSchedDsRead = 0x100;
+// fp8 caches: a wave stages each step's 16 rows of codes in LDS, two steps at a time
+constexpr int kSRow = kDK + 16;          // stage row stride in bytes (592)
+constexpr int kStageB = kStep * kSRow + 128;  // second stage of a pair (9,600 B in)
+constexpr int kPairBytes = 19200;        // a wave's pair of stages
 
 struct DecodeSmem {
   union {
-    uint16_t v[kWaves][2 * kStep * kVRow];  // 135,168 B: two value tiles per wave
+    uint16_t v[kWaves][2 * kStep * kVRow];  // 135,168 B: two value tiles per wave (bf16)
+    uint8_t st[kWaves][kPairBytes];         //  76,800 B: a pair of step stages per wave (fp8)
     struct {
       float o[kWaves][16 * kORow];          // 132,096 B: each wave's scaled accumulator
       float m[kWaves][16];
@@ -281,50 +292,17 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     // through the scalar cache and stays out of the vector-load queue: a vector load
     // here would make every later wait on it drain the whole prefetch ring.
     const kconst_i32* bt = (const kconst_i32*)(p.block_table + (size_t)b * p.max_blocks);
+    int ids_seen = 0;  // OR of the block ids read: negative if one was (flagged after the loop)
     auto step_row = [&](int t0) -> long {
       t0 = __builtin_amdgcn_readfirstlane(t0);
-      return block_id(p, bt, t0 / p.block_size) * p.block_size + t0 % p.block_size;
+      const long id = kFp8 ? block_id(bt, t0 / p.block_size, ids_seen)
+                           : block_id_now(p, bt, t0 / p.block_size);
+      return id * p.block_size + t0 % p.block_size;
     };
-    auto load_step = [&](long row0, int t0, u32x4* dst) {
-      // all 16 tokens of an aligned step sit in one block; clamping into the visible
-      // span keeps every lane inside the step, on a real row, never a poisoned slot
-      const int t = min(max(t0 + col, lo), hi_all - 1);
-      const uint8_t* krow = p.kv + row0 * row_bytes + (t - t0) * (int)row_bytes;
-  #pragma unroll
-      for (int i = 0; i < kLoads; ++i)
-        dst[i] = *(const u32x4*)(krow + (kFp8 ? 64 * i + 16 * grp : 2 * kdim(i, grp)));
-    };
-
-    // Score half of a step: the keys of step t0 (raw cache bytes) against the row
-    // block's queries.  Lane (col, grp) gets tokens t0 + 4 grp + i of query row col;
-    // the value part of each fragment goes to LDS tile `vt_w` on the way (bf16,
-    // token-major).  Returns P^T as the B operand of the value MFMA.
-    auto score_step = [&](const u32x4* raw, int t0, uint16_t* vt_w) -> i16x4 {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-      // write bases: chunk 8 j + 2 grp + h of row col sits at chunk (8 j + 2 grp + (h ^ sw))
-      const int sw = (col >> 3) & 1;
-      uint16_t* vrow0 = vt_w + col * kVRow + 16 * grp + 8 * sw;        // h = 0
-      uint16_t* vrow1 = vt_w + col * kVRow + 16 * grp + 8 * (sw ^ 1);  // h = 1
-      if constexpr (kFp8) {
-  #pragma unroll
-        for (int j = 0; j < 9; ++j) {
-          bf16x8 ka, kb;
-          fp8x16_to_bf16(raw[j], ka, kb);
-          if (j < 8) {  // dims 64 j + 16 grp .. + 15 are chunks 8 j + 2 grp, + 1
-            *(bf16x8*)(vrow0 + 64 * j) = ka;
-            *(bf16x8*)(vrow1 + 64 * j) = kb;
-          }
-          sc = mfma_16x16x32(ka, qfrag(2 * j), sc);
-          sc = mfma_16x16x32(kb, qfrag(2 * j + 1), sc);
-        }
-      } else {
-  #pragma unroll
-        for (int kk = 0; kk < kKSteps; ++kk) {
-          const bf16x8 k = __builtin_bit_cast(bf16x8, raw[kk]);
-          if (kk < 16) *(bf16x8*)(((kk & 1) ? vrow1 : vrow0) + 64 * (kk >> 1)) = k;
-          sc = mfma_16x16x32(k, qfrag(kk), sc);
-        }
-      }
+    // Masking and the softmax numerator of one step's scores: lane (col, grp) holds
+    // S^T[tokens t0 + 4 grp + i][query row col].  Returns the bf16 weights, which are
+    // the value MFMA's B operand as they stand.
+    auto weigh = [&](f32x4 sc, int t0) -> bf16x4 {
       float sv[4];
       float cm = -INFINITY;
   #pragma unroll
@@ -351,7 +329,36 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
       const bf16x4 pb = {(__bf16)pv[0], (__bf16)pv[1], (__bf16)pv[2], (__bf16)pv[3]};
   #pragma unroll
       for (int i = 0; i < 4; ++i) lb_run += (float)pb[i];
-      return __builtin_bit_cast(i16x4, pb);
+      return pb;
+    };
+
+    // BF16 caches.  Lanes load their MFMA fragments straight from the cache.
+    auto load_step = [&](long row0, int t0, u32x4* dst) {
+      // all 16 tokens of an aligned step sit in one block; clamping into the visible
+      // span keeps every lane inside the step, on a real row, never a poisoned slot
+      const int t = min(max(t0 + col, lo), hi_all - 1);
+      const uint8_t* krow = p.kv + row0 * row_bytes + (t - t0) * (int)row_bytes;
+  #pragma unroll
+      for (int i = 0; i < kLoads; ++i) dst[i] = *(const u32x4*)(krow + 2 * kdim(i, grp));
+    };
+
+    // Score half of a step: the keys of step t0 (raw cache bytes) against the row
+    // block's queries.  Lane (col, grp) gets tokens t0 + 4 grp + i of query row col;
+    // the value part of each fragment goes to LDS tile `vt_w` on the way (bf16,
+    // token-major).  Returns P^T as the B operand of the value MFMA.
+    auto score_step = [&](const u32x4* raw, int t0, uint16_t* vt_w) -> i16x4 {
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      // write bases: chunk 8 j + 2 grp + h of row col sits at chunk (8 j + 2 grp + (h ^ sw))
+      const int sw = (col >> 3) & 1;
+      uint16_t* vrow0 = vt_w + col * kVRow + 16 * grp + 8 * sw;        // h = 0
+      uint16_t* vrow1 = vt_w + col * kVRow + 16 * grp + 8 * (sw ^ 1);  // h = 1
+  #pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        const bf16x8 k = __builtin_bit_cast(bf16x8, raw[kk]);
+        if (kk < 16) *(bf16x8*)(((kk & 1) ? vrow1 : vrow0) + 64 * (kk >> 1)) = k;
+        sc = mfma_16x16x32(k, qfrag(kk), sc);
+      }
+      return __builtin_bit_cast(i16x4, weigh(sc, t0));
     };
 
     // Value half of a step: O^T += V^T P^T from LDS tile `vt_r`, read transposed.
@@ -360,39 +367,118 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     const int v_lane = vr * kVRow + 8 * (((col & 3) >> 1) ^ ((vr >> 3) & 1)) + 4 * (col & 1);
     auto pv_step = [&](const uint16_t* vt_r, i16x4 pf) {
       const uint16_t* vsrc = vt_r + v_lane;
-      // The transposed reads run kAheadV MFMAs ahead (all 32 for fp8 caches, 8 for
-      // bf16, whose larger register ring leaves less room), so the LDS latency is paid
+      // The transposed reads run kAheadV MFMAs ahead, so the LDS latency is paid
       // about once per step rather than once per MFMA.
-      constexpr int kAheadV = kFp8 ? 32 : 8;
+      constexpr int kAheadV = 8;
       i16x4 vf[32];
   #pragma unroll
       for (int m = 0; m < 32; ++m) vf[m] = lds_read_tr16(vsrc + 16 * m);
   #pragma unroll
       for (int m = 0; m < 32; ++m) acc[m] = mfma_16x16x16(vf[m], pf, acc[m]);
-      constexpr int kDsRead = 0x100, kMfma = 0x8;
-      __builtin_amdgcn_sched_group_barrier(kDsRead, kAheadV, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kAheadV, 0);
   #pragma unroll
       for (int m = 0; m < 32 - kAheadV; ++m) {
-        __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(kMfma, kAheadV, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, kAheadV, 0);
     };
 
-    // The two halves are software-pipelined: while the value MFMAs of step i run,
-    // the same wave widens, stores and scores step i + 1 (two LDS value tiles per
-    // wave alternate), so the matrix pipe is not idle through the conversion,
-    // softmax and LDS round trips of one step.  A ring of kDepth register buffers
-    // keeps the loads of the next steps in flight (one step moves 9 KB of fp8 or
-    // 18 KB of bf16 rows per wave); the loop is unrolled by kDepth so every buffer
-    // index is a compile-time constant.
-    constexpr int kDepth = kFp8 ? 3 : 2;
+    // FP8 caches.  A step's 16 rows are 9,216 contiguous bytes, which every lane
+    // loads as 16-byte pieces of whole 1 KB spans with the nontemporal hint (each
+    // wave-wide load a run of full 128-byte lines: measured 6.2 - 6.5 TB/s, against
+    // 5.7 - 5.8 for the fragment layout's 64-byte halves of lines, which the hint
+    // only slows), and writes as they stand to a stage of 16 padded rows in LDS.
+    // The score fragments are read back from the stage in the MFMA layout, and the
+    // value operand with transposed 8-bit reads, widened to bf16 after the read;
+    // only visible rows are read (row indices clamped into the span, as above), so
+    // whatever the rows past a sequence's end hold never reaches the arithmetic.
+    // Rows are 592 bytes apart and a pair's second stage starts 128 bytes (mod 256)
+    // after the first: the 16 fragment reads of a 16-lane phase fall in 16 distinct
+    // 16-byte bank groups, and a transposed read's 32 rows in distinct banks.
+    uint8_t* const stA = sm.st[wave];
+    uint8_t* const stB = stA + kStageB;
+    auto load_codes = [&](long row0, u32x4* dst) {
+      const u32x4* src = (const u32x4*)(p.kv + row0 * kDK) + lane;
+  #pragma unroll
+      for (int i = 0; i < 9; ++i) dst[i] = __builtin_nontemporal_load(src + 64 * i);
+    };
+    // Score half: stage the codes of step t0, read back the lane's key fragments
+    // (token t0 + col, dims 64 j + 16 grp .. + 15), widen and score them.
+    auto stage_score = [&](const u32x4* raw, int t0, uint8_t* stage) -> bf16x4 {
+  #pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        const int u = 64 * i + lane;  // 16-byte piece u of the step: token u / 36
+        *(u32x4*)(stage + (u / 36) * kSRow + 16 * (u % 36)) = raw[i];
+      }
+      wave_lds_fence();
+      const int tk = min(max(t0 + col, lo), hi_all - 1) - t0;
+      const uint8_t* kb = stage + tk * kSRow + 16 * grp;
+      u32x4 kw[9];
+  #pragma unroll
+      for (int j = 0; j < 9; ++j) kw[j] = *(const u32x4*)(kb + 64 * j);
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        bf16x8 ka, kb2;
+        fp8x16_to_bf16(kw[j], ka, kb2);
+        sc = mfma_16x16x32(ka, qfrag(2 * j), sc);
+        sc = mfma_16x16x32(kb2, qfrag(2 * j + 1), sc);
+      }
+      // all nine reads first (left alone, the compiler waits for each read right
+      // before its MFMAs: nine LDS round trips per step), then each fragment's
+      // widening and its two MFMAs
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 9, 0);
+  #pragma unroll
+      for (int j = 0; j < 9; ++j) {
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+      }
+      return weigh(sc, t0);
+    };
+    // Value half of a pair of steps (t0a in stage A, t0b in stage B): O^T += V^T P^T
+    // over their 32 tokens with 32 MFMA 16x16x32.  The MFMA's contraction index
+    // 8 grp + e stands for token t0a + 4 grp + e (e < 4) or t0b + 4 grp + e - 4
+    // (e >= 4), which is where the two steps' scores sit in P.  A transposed read gives
+    // lane (col, grp) dim 16 m + col of the 8 tokens whose half-rows lanes 2 e and
+    // 2 e + 1 of its group address.  Without a second step (pb = 0) the B half reads
+    // stage A's rows again, finite values under zero weights.
+    const int ve = col >> 1;
+    auto stage_value = [&](int t0a, int t0b, bool has_b, bf16x4 pa, bf16x4 pb) {
+      const bool in_b = has_b && ve >= 4;
+      const int t0x = in_b ? t0b : t0a;
+      const int tv = min(max(t0x + 4 * grp + (ve & 3), lo), hi_all - 1) - t0x;
+      const uint8_t* vsrc = (in_b ? stB : stA) + tv * kSRow + 8 * (col & 1);
+      const bf16x8 pf = __builtin_shufflevector(pa, pb, 0, 1, 2, 3, 4, 5, 6, 7);
+      // The transposed reads run kAhead MFMAs ahead of their use, in a register ring
+      // whose order a scheduling barrier per MFMA pins (left alone, the compiler
+      // issues each read right before its widening and waits for it).
+      constexpr int kAhead = 8;
+      u32x2 vf[kAhead];
+  #pragma unroll
+      for (int m = 0; m < kAhead; ++m) vf[m] = lds_read_tr8(vsrc + 16 * m);
+  #pragma unroll
+      for (int m = 0; m < 32; ++m) {
+        const bf16x8 v = fp8x8_to_bf16(vf[m % kAhead]);
+        if (m + kAhead < 32) vf[m % kAhead] = lds_read_tr8(vsrc + 16 * (m + kAhead));
+        acc[m] = mfma_16x16x32(v, pf, acc[m]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+
+    // A ring of two register buffers keeps the next step's loads in flight while a
+    // step computes (one step moves 9 KB of fp8 or 18 KB of bf16 rows per wave).
+    // BF16: the halves are software-pipelined: while the value MFMAs of step i run,
+    // the same wave stores and scores step i + 1 (two LDS value tiles per wave
+    // alternate).  FP8: steps go in pairs, each staged and scored in turn, then the
+    // pair's values.
+    constexpr int kDepth = 2;
     constexpr int kStride = kStep * kWaves;
     const int t_first = sr.base + kStep * (a + wave);
     const int n_steps = a + wave < e ? (e - a - wave + kWaves - 1) / kWaves : 0;
     // Every iteration issues the same loads (prefetches past the wave's last step
-    // re-read that step), so the compiler counts them exactly and keeps the whole
-    // ring in flight.
+    // re-read that step), so the compiler counts them exactly and keeps the ring in
+    // flight.
     u32x4 ring[kDepth][kLoads];
     const int last_t0 = t_first + (n_steps - 1) * kStride;
     auto step_t0 = [&](int i) { return min(t_first + i * kStride, last_t0); };
@@ -404,38 +490,60 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     lb_run = 0.f;
     if (n_steps > 0) {
       long row_next;  // cache row of the step the next prefetch loads (read a step early)
+      if constexpr (kFp8) {
+        load_codes(step_row(step_t0(0)), ring[0]);
+        load_codes(step_row(step_t0(1)), ring[1]);
+        row_next = step_row(step_t0(2));
+        for (int i = 0; i < n_steps; i += 2) {
+          const int ta = t_first + i * kStride, tb = ta + kStride;
+          const bool has_b = i + 1 < n_steps;
+          const bf16x4 pa = stage_score(ring[0], ta, stA);
+          load_codes(row_next, ring[0]);  // step i + 2
+          row_next = step_row(step_t0(i + 3));
+          __builtin_amdgcn_sched_barrier(0);
+          bf16x4 pb = {};
+          if (has_b) pb = stage_score(ring[1], tb, stB);
+          load_codes(row_next, ring[1]);  // step i + 3
+          row_next = step_row(step_t0(i + 4));
+          __builtin_amdgcn_sched_barrier(0);
+          stage_value(ta, tb, has_b, pa, pb);
+          wave_lds_fence();
+        }
+      } else {
   #pragma unroll
-      for (int u = 0; u < kDepth; ++u) load_step(step_row(step_t0(u)), step_t0(u), ring[u]);
-      row_next = step_row(step_t0(kDepth));
-      i16x4 pf = score_step(ring[0], t_first, tile(0));
-      wave_lds_fence();
-      // iteration i: prefetch step i + kDepth into the slot step i left, score step
-      // i + 1, accumulate step i
-      auto body = [&](int i, const u32x4* raw_next, u32x4* slot_free) {
-        load_step(row_next, step_t0(i + kDepth), slot_free);
-        row_next = step_row(step_t0(i + kDepth + 1));
-        __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the step computes
-        const i16x4 pf_next = score_step(raw_next, t_first + (i + 1) * kStride, tile(i + 1));
-        pv_step(tile(i), pf);
-        pf = pf_next;
+        for (int u = 0; u < kDepth; ++u) load_step(step_row(step_t0(u)), step_t0(u), ring[u]);
+        row_next = step_row(step_t0(kDepth));
+        i16x4 pf = score_step(ring[0], t_first, tile(0));
         wave_lds_fence();
-      };
-      int i0 = 0;
-      for (; i0 + kDepth < n_steps; i0 += kDepth) {
+        // iteration i: prefetch step i + kDepth into the slot step i left, score step
+        // i + 1, accumulate step i
+        auto body = [&](int i, const u32x4* raw_next, u32x4* slot_free) {
+          load_step(row_next, step_t0(i + kDepth), slot_free);
+          row_next = step_row(step_t0(i + kDepth + 1));
+          __builtin_amdgcn_sched_barrier(0);  // the prefetch is issued before the step computes
+          const i16x4 pf_next = score_step(raw_next, t_first + (i + 1) * kStride, tile(i + 1));
+          pv_step(tile(i), pf);
+          pf = pf_next;
+          wave_lds_fence();
+        };
+        int i0 = 0;
+        for (; i0 + kDepth < n_steps; i0 += kDepth) {
   #pragma unroll
-        for (int u = 0; u < kDepth; ++u) body(i0 + u, ring[(u + 1) % kDepth], ring[u]);
+          for (int u = 0; u < kDepth; ++u) body(i0 + u, ring[(u + 1) % kDepth], ring[u]);
+        }
+  #pragma unroll
+        for (int u = 0; u < kDepth - 1; ++u)
+          if (i0 + u + 1 < n_steps) body(i0 + u, ring[(u + 1) % kDepth], ring[u]);
+        pv_step(tile(n_steps - 1), pf);
+        wave_lds_fence();
       }
-  #pragma unroll
-      for (int u = 0; u < kDepth - 1; ++u)
-        if (i0 + u + 1 < n_steps) body(i0 + u, ring[(u + 1) % kDepth], ring[u]);
-      pv_step(tile(n_steps - 1), pf);
-      wave_lds_fence();
     }
     // a row beyond its cap: run the steps again from its true maximum
     if (!__builtin_amdgcn_ballot_w64(m_max > m_ref + kCap)) break;
     // only the rows that went past their cap move; the others recompute bit-identically
     m_ref = (m_max > m_ref + kCap) ? m_max : m_ref;
     }
+    if (kFp8 && ids_seen < 0 && lane == 0) raise_flag(p, kFlagBadBlocks);
 
     MLA_STAMP(decode_stamps, 2);
     // ---- merge the four waves: one round through LDS ----

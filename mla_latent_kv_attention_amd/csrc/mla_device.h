@@ -5,7 +5,10 @@
 // (l / 16) + i], B[(K/4) * (l / 16) + i][l % 16], and the 16x16 f32 result
 // C[4 * (l / 16) + i][l % 16].  The LDS transpose read ds_read_b64_tr_b16
 // works on 16-lane groups: lane j of a group receives element (j % 4) of the
-// 8-byte chunk addressed by lane (4 * s + j / 4), for s = 0..3.
+// 8-byte chunk addressed by lane (4 * s + j / 4), for s = 0..3.  Its 8-bit form
+// ds_read_b64_tr_b8 likewise: lane j of a group receives byte j % 8 of the chunk
+// addressed by lane (2 * s + j / 8), for s = 0..7, i.e. the group's 8 chunk pairs
+// are 8 rows of 16 bytes and lane j gets column j of all 8.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -28,6 +31,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
 
 // S += A (16 x 32) * B (32 x 16), bf16 in, fp32 accumulate.
 __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -44,10 +49,23 @@ __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
 }
 
+// Transposed 8 x 8-bit LDS read (see the layout note at the top).
+__device__ __forceinline__ u32x2 lds_read_tr8(const void* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(p)));
+}
+
 // Exact OCP E4M3FN -> bf16 for four codes packed in one dword (bytes 0..3).
 __device__ __forceinline__ void fp8x4_to_bf16(uint32_t w, bf16x2& lo, bf16x2& hi) {
   lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false);
   hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true);
+}
+
+// 8 FP8 codes -> bf16x8, exact.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(u32x2 w) {
+  bf16x2 p0, p1, p2, p3;
+  fp8x4_to_bf16(w.x, p0, p1);
+  fp8x4_to_bf16(w.y, p2, p3);
+  return (bf16x8){p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // 16 FP8 codes -> two bf16x8 (codes 0..7, codes 8..15), exact.

@@ -146,9 +146,19 @@ __device__ __forceinline__ void check_lengths(const DecodeParams& p, int b) {
 
 // Physical block of logical block i in a sequence's block-table row bt (a uniform
 // index: the id comes through the scalar cache).  A negative id, outside the
-// contract, would address memory before the cache: block 0 is read instead and the
-// call is flagged.
-__device__ __forceinline__ long block_id(const DecodeParams& p, const kconst_i32* bt, int i) {
+// contract, would address memory before the cache: block 0 is read instead, and the
+// ids are OR-ed into `seen`, whose sign bit the caller checks to flag the call once its
+// loop is done (a branch here would make every block-id load wait at once).
+__device__ __forceinline__ long block_id(const kconst_i32* bt, int i, int& seen) {
+  const int id = bt[i];
+  seen |= id;
+  return id < 0 ? 0 : id;
+}
+
+// The same with the flag raised at once.  (In the bf16 decode kernel the deferred
+// form above changes the register allocation enough to spill; there this one is
+// kept.)
+__device__ __forceinline__ long block_id_now(const DecodeParams& p, const kconst_i32* bt, int i) {
   const int id = bt[i];
   if (id < 0) {
     raise_flag(p, kFlagBadBlocks);

@@ -237,6 +237,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
     // masked tokens' scores are discarded).  A half wholly past the range reads the
     // range's last row.
     const kconst_i32* bt = (const kconst_i32*)(p.block_table + (size_t)b * p.max_blocks);
+    int ids_seen = 0;  // OR of the block ids read: negative if one was (flagged after the loop)
     const int n_tiles = (e - a + 1) / 2;
     const int tend = sr.base + kStep * e;  // tokens from here on belong to the next piece
     auto tile_t0 = [&](int k) { return sr.base + kStep * (a + 2 * k); };
@@ -249,7 +250,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       const int hb = th < hi_all ? th : ((hi_all - 1) & ~(kStep - 1));
       Half h;
       h.hb = hb;
-      h.row0 = block_id(p, bt, hb / p.block_size) * p.block_size + hb % p.block_size;
+      h.row0 = block_id(bt, hb / p.block_size, ids_seen) * p.block_size + hb % p.block_size;
       return h;
     };
     // byte address of token t's 16-byte chunk pc, for a token of half h
@@ -480,6 +481,7 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
       if (!rerun) break;
       m_ref = (m_max > m_ref + kCap) ? m_max : m_ref;
     }
+    if (ids_seen < 0 && tid == 0) raise_flag(p, kFlagBadBlocks);
 
     MLA_STAMP(verify_stamps, 5);
     // ---- normalisers: the owners publish each row's, every wave scales its dims ----
