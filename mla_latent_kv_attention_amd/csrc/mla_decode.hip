@@ -398,8 +398,11 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     // 16-byte bank groups, and a transposed read's 32 rows in distinct banks.
     uint8_t* const stA = sm.st[wave];
     uint8_t* const stB = stA + kStageB;
-    auto load_codes = [&](long row0, u32x4* dst) {
-      const u32x4* src = (const u32x4*)(p.kv + row0 * kDK) + lane;
+    // A prefetch past the wave's last step (live false) still issues its loads, so the
+    // waits stay exact, but every lane reads the same 16 bytes: one small request per
+    // load instead of a re-read of the last step.
+    auto load_codes = [&](long row0, u32x4* dst, bool live) {
+      const u32x4* src = (const u32x4*)(p.kv + row0 * kDK) + (live ? lane : 0);
   #pragma unroll
       for (int i = 0; i < 9; ++i) dst[i] = __builtin_nontemporal_load(src + 64 * i);
     };
@@ -491,19 +494,19 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     if (n_steps > 0) {
       long row_next;  // cache row of the step the next prefetch loads (read a step early)
       if constexpr (kFp8) {
-        load_codes(step_row(step_t0(0)), ring[0]);
-        load_codes(step_row(step_t0(1)), ring[1]);
+        load_codes(step_row(step_t0(0)), ring[0], true);
+        load_codes(step_row(step_t0(1)), ring[1], n_steps > 1);
         row_next = step_row(step_t0(2));
         for (int i = 0; i < n_steps; i += 2) {
           const int ta = t_first + i * kStride, tb = ta + kStride;
           const bool has_b = i + 1 < n_steps;
           const bf16x4 pa = stage_score(ring[0], ta, stA);
-          load_codes(row_next, ring[0]);  // step i + 2
+          load_codes(row_next, ring[0], i + 2 < n_steps);  // step i + 2
           row_next = step_row(step_t0(i + 3));
           __builtin_amdgcn_sched_barrier(0);
           bf16x4 pb = {};
           if (has_b) pb = stage_score(ring[1], tb, stB);
-          load_codes(row_next, ring[1]);  // step i + 3
+          load_codes(row_next, ring[1], i + 3 < n_steps);  // step i + 3
           row_next = step_row(step_t0(i + 4));
           __builtin_amdgcn_sched_barrier(0);
           stage_value(ta, tb, has_b, pa, pb);
