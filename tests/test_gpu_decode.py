@@ -76,11 +76,27 @@ def test_explicit_split_counts(mla, num_splits):
     check_lse(lse, ref_l)
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("block_size", [16, 48, 64, 256])
-def test_block_sizes(mla, block_size):
-    q, cache = small_case(2002, [1, 100, 700], 12, 1, "bf16", block_size=block_size)
+def test_block_sizes(mla, block_size, kv_dtype):
+    q, cache = small_case(2002, [1, 100, 700], 12, 1, kv_dtype, block_size=block_size)
     out, lse = run_gpu(mla, q, cache)
     ref_o, ref_l = run_oracle(q, cache)
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+
+
+@pytest.mark.parametrize("num_splits", [0, 9, 40])
+def test_fp8_steps_and_starts_inside_steps(mla, num_splits):
+    """FP8 caches load whole 16-token steps, poisoned rows past a sequence's end
+    included, and take steps in pairs: lengths and key ranges that start and end inside
+    a step, with piece counts that leave waves zero, one, two or more steps (an unpaired
+    last step, prefetches past a wave's end), every row against the oracle."""
+    lens = [2, 15, 16, 17, 47, 63, 64, 65, 130, 257, 1001]
+    kb = np.array([0, 3, 0, 9, 1, 62, 0, 33, 100, 0, 517], np.int32)
+    q, cache = small_case(2020, lens, 12, 2, "fp8", block_size=16)
+    out, lse = run_gpu(mla, q, cache, kv_begin=kb, num_splits=num_splits)
+    ref_o, ref_l = run_oracle(q, cache, kb)
     check_out(out, ref_o)
     check_lse(lse, ref_l)
 
