@@ -687,12 +687,17 @@ __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p)
     f32x4 t[kBatch][kVec];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int v = min(v0 + 8 * u, w_last);  // past the end: re-read, weight 0
-      l4[u] = (v0 + 8 * u <= w_last) ? lse_b[v * R] : -INFINITY;
-      const f32x4* src =
-          (const f32x4*)(p.part_out + ((size_t)(v + b) * R + rr) * kDV + d0 + 4 * kVec * l);
+      const int v = v0 + 8 * u;
+      l4[u] = -INFINITY;
 #pragma unroll
-      for (int k = 0; k < kVec; ++k) t[u][k] = src[k];
+      for (int k = 0; k < kVec; ++k) t[u][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+      if (v <= w_last) {  // past the end: no load, weight 0
+        l4[u] = lse_b[v * R];
+        const f32x4* src =
+            (const f32x4*)(p.part_out + ((size_t)(v + b) * R + rr) * kDV + d0 + 4 * kVec * l);
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) t[u][k] = src[k];
+      }
     }
     float m_new = mx;
 #pragma unroll
