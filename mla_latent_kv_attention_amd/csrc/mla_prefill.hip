@@ -11,15 +11,19 @@
 // sequence; each of its four waves owns 32 of them, with the waves' Q^T
 // fragments held in registers for the whole key loop (36 x 8 bf16 per lane).
 // The work-group walks the sequence's keys in 32-token tiles up to its last
-// row's token; each tile is staged once in LDS (bf16, padded rows; fp8 caches
-// widened exactly on the way in) with the next tile's loads in flight, and
-// read by all four waves:
-//   S^T[32 tokens x 32 rows] = K Q^T           36 MFMA 32x32x16 (A from LDS)
+// row's token; each tile is copied once into an LDS ring as the cache holds it
+// (bf16, or fp8 codes: padded rows, 1 KB global->LDS copies, two tiles in flight)
+// and read by all four waves:
+//   S^T[32 tokens x 32 rows] = K Q^T           36 MFMA 32x32x16 (A from LDS; fp8
+//                                               codes 16 per read, widened exactly
+//                                               after the read)
 //   causal mask, online softmax against a per-row reference fixed from the first
 //   tile before the key loop
 //   O^T[512 x 32 rows] += V^T P^T               32 MFMA 32x32x16 (A = V^T read
-//                                               with ds_read_b64_tr_b16, B = P^T
-//                                               straight from the score registers)
+//                                               with ds_read_b64_tr_b16, or for fp8
+//                                               with ds_read_b64_tr_b8 and widened;
+//                                               B = P^T straight from the score
+//                                               registers)
 // Work-groups are launched longest-first (the last rows of a sequence see the
 // most keys), and consecutive ids fan out over the 8 XCDs, so every XCD works
 // on a mix of long and short rows that all stream the same leading key tiles.
@@ -37,41 +41,47 @@ constexpr int kRowsPerWg = 128;
 constexpr int kRowsPerWave = 32;
 constexpr int kTile = 32;                        // key tokens per tile
 constexpr int kKSteps = 36;                      // 576 / 16
-constexpr int kRowBytes = 2 * kDK;               // 1152: one bf16 latent row
-constexpr int kPRowChunks = kRowBytes / 16 + 1;  // 73 16-byte chunks: 72 of data + 1 pad
-constexpr int kPRow = 8 * kPRowChunks;           // padded LDS row (bf16 elements)
-constexpr int kTileElems = kTile * kPRow;
-constexpr int kDmaPerWave = 10;                  // copies per wave and tile (the last repeats)
-constexpr int kDmaBlocks = 37;                   // 1 KB blocks that cover a padded tile
-constexpr int kSlotBytes = kDmaBlocks * 1024;
-constexpr int kRing = 4;                         // bf16 tiles: two in use, two in flight
+constexpr int kRing = 4;                         // tiles: two in use, two in flight
 constexpr float kCap = 64.0f;  // log2 units a score may exceed its row's reference max
 constexpr int kKAhead = 3;     // K fragments read this many score MFMAs ahead
 constexpr int kVAhead = 3;     // V^T operands read this many value MFMAs ahead
 
-static_assert(kTile * kPRowChunks <= kDmaBlocks * 64, "DMA slots must cover a tile");
-static_assert(4 * kDmaPerWave >= kDmaBlocks, "the waves' copies must cover every block");
+// LDS layout of a tile: 32 rows of the cache's codes as they stand (bf16, or fp8 for
+// fp8 caches), each padded by one 16-byte chunk, filled by 1 KB global->LDS copies.
+template <bool kFp8>
+struct Layout {
+  static constexpr int kRowBytes = kFp8 ? kDK : 2 * kDK;             // 576 / 1152
+  static constexpr int kPRowChunks = kRowBytes / 16 + 1;             // 37 / 73: data + 1 pad
+  static constexpr int kPRowBytes = 16 * kPRowChunks;                // 592 / 1168
+  static constexpr int kDmaBlocks = (kTile * kPRowChunks + 63) / 64; // 19 / 37 1 KB blocks
+  static constexpr int kDmaPerWave = (kDmaBlocks + 3) / 4;           // 5 / 10 (the last repeats)
+  static constexpr int kSlotBytes = kDmaBlocks * 1024;
+  static_assert(kTile * kPRowChunks <= kDmaBlocks * 64, "DMA slots must cover a tile");
+  static_assert(4 * kDmaPerWave >= kDmaBlocks, "the waves' copies must cover every block");
+};
 
 // Copy key tile [tok0, tok0 + 32) of a sequence into an LDS slot laid out as
-// 32 padded rows of 73 chunks.  Chunk positions past the tile land in the slot's
-// slack; pad chunks and rows past the sequence end get real (masked) rows.
-// seq_kv points at the sequence's first latent row.
+// 32 padded rows.  Chunk positions past the tile land in the slot's slack; pad chunks
+// and rows past the sequence end get real (masked) rows.  seq_kv points at the
+// sequence's first latent row.
+template <bool kFp8>
 __device__ __forceinline__ void dma_tile(const uint8_t* seq_kv, int len, int tok0, uint32_t slot,
                                          int wave, int lane) {
+  using L = Layout<kFp8>;
   // keep the per-lane chunk coordinates out of loop-invariant code motion: ten
   // of them held across the key loop would cost 20 VGPRs
   int l = lane;
   asm volatile("" : "+v"(l));
 #pragma unroll
-  for (int i = 0; i < kDmaPerWave; ++i) {
+  for (int i = 0; i < L::kDmaPerWave; ++i) {
     // block wave + 4 i; the waves' spare copies repeat the last block (same bytes)
-    const int inst = min(wave + 4 * i, kDmaBlocks - 1);
+    const int inst = min(wave + 4 * i, L::kDmaBlocks - 1);
     const int pos = 64 * inst + l;
-    int row = pos / kPRowChunks, pc = pos - row * kPRowChunks;
+    int row = pos / L::kPRowChunks, pc = pos - row * L::kPRowChunks;
     if (row >= kTile) row = kTile - 1;
-    if (pc == kPRowChunks - 1) pc = 0;
+    if (pc == L::kPRowChunks - 1) pc = 0;
     const int t = min(tok0 + row, len - 1);
-    dma16(seq_kv, (uint32_t)(t * kRowBytes + 16 * pc), slot + 1024 * inst);
+    dma16(seq_kv, (uint32_t)(t * L::kRowBytes + 16 * pc), slot + 1024 * inst);
   }
 }
 
@@ -79,48 +89,12 @@ __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// FP8 tiles go through registers: 16 codes per 16-byte load, widened exactly to
-// bf16 on the way into the same padded LDS layout.
-struct Fp8Stage {
-  static constexpr int kRowChunks = kDK / 16;  // 36
-  static constexpr int kTotal = kTile * kRowChunks;
-  static constexpr int kChunks = (kTotal + 255) / 256;
-  u32x4 r[kChunks];
-
-  __device__ __forceinline__ void load(const uint8_t* kv, int seq_start, int len, int tok0,
-                                       int tid) {
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      const int c = tid + 256 * k;
-      if (c < kTotal) {
-        const int row = c / kRowChunks, cc = c % kRowChunks;
-        const int t = min(tok0 + row, len - 1);  // rows past the sequence end are masked
-        r[k] = *(const u32x4*)(kv + ((size_t)(seq_start + t) * kRowChunks + cc) * 16);
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* buf, int tid) const {
-#pragma unroll
-    for (int k = 0; k < kChunks; ++k) {
-      const int c = tid + 256 * k;
-      if (c < kTotal) {
-        const int row = c / kRowChunks, cc = c % kRowChunks;
-        bf16x8 lo, hi;
-        fp8x16_to_bf16(r[k], lo, hi);
-        *(bf16x8*)(buf + row * kPRow + 16 * cc) = lo;
-        *(bf16x8*)(buf + row * kPRow + 16 * cc + 8) = hi;
-      }
-    }
-  }
-};
-
 template <bool kFp8>
 __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) {
-  // fp8 tiles are staged through registers, which leaves room for a shallower ring
-  // (measured: 12.6 ms at depth 2 against 14.3 ms at depth 3 on the 32,768-token shape)
-  constexpr int KA = kFp8 ? 2 : kKAhead, VA = kFp8 ? 2 : kVAhead;
-  // bf16: a ring of 4 DMA slots (148 KB); fp8: two register-staged tiles (73 KB)
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kFp8 ? 2 * kTileElems : kRing * kSlotBytes / 2];
+  using L = Layout<kFp8>;
+  constexpr int KA = kKAhead, VA = kVAhead;
+  // a ring of 4 tile slots: 148 KB of bf16 rows, 76 KB of fp8 codes
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kRing * L::kSlotBytes];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -147,16 +121,21 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   const int wg_first_tok = row0 / p.H;
   const int n_tiles = wg_last_tok / kTile + 1;
 
-  // ---- this lane's query row and its Q^T fragments (B operand, 8 dims per k-step)
+  // ---- this lane's query row and its Q^T fragments (B operand, 8 dims per k-step).
+  // k-step kk covers dims 16 kk .. + 15, lane group g eight of them; for fp8 tiles,
+  // whose fragments come 16 codes per read, k-steps 2 j and 2 j + 1 cover dims
+  // 32 j .. + 31 with lane group g holding 32 j + 16 g + 8 (kk % 2) .. + 7 (the same
+  // permutation of the contraction index on both sides).
   const int r = row0 + kRowsPerWave * wave + n;
   const bool row_ok = r < rows;
   const int tq = row_ok ? r / p.H : -1;  // causal limit: keys 0 .. tq
   bf16x8 qf[kKSteps];
   {
-    const uint16_t* qrow = p.q + ((size_t)seq_start * p.H + (row_ok ? r : 0)) * kDK + 8 * g;
+    const uint16_t* qrow =
+        p.q + ((size_t)seq_start * p.H + (row_ok ? r : 0)) * kDK + (kFp8 ? 16 : 8) * g;
 #pragma unroll
     for (int kk = 0; kk < kKSteps; ++kk) {
-      bf16x8 v = *(const bf16x8*)(qrow + 16 * kk);
+      bf16x8 v = *(const bf16x8*)(qrow + (kFp8 ? 32 * (kk >> 1) + 8 * (kk & 1) : 16 * kk));
       qf[kk] = row_ok ? v : (bf16x8){};
     }
   }
@@ -180,10 +159,18 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   float l_run = 0.f;   // sum of the fp32 probabilities: the lse
   float lb_run = 0.f;  // sum of their bf16 roundings: the output's normaliser
 
-  // per-lane LDS offsets (elements) inside a tile
-  const int a_off = n * kPRow + 8 * g;  // K fragment: token n, dims 16 kk + 8 g
-  const int v_tok = 4 * g + ((lane & 15) >> 2);
-  int v_off = v_tok * kPRow + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // per-lane LDS byte offsets inside a tile.  K fragment: token n, byte 16 g of each
+  // 32-byte step (bf16: dims 16 kk + 8 g; fp8: the 16 codes of dims 32 j + 16 g).
+  const int a_off = n * L::kPRowBytes + 16 * g;
+  // V^T: bf16, lane (l & 15) of a 16-lane group addresses token 4 g + (l & 15) / 4,
+  // dims 4 (l & 3) .. + 3 of the group's 16 (ds_read_b64_tr_b16, second read 8 tokens
+  // on); fp8, it addresses half-row (l & 1) of token 8 (e / 4) + 4 g + e % 4,
+  // e = (l & 15) / 2 (ds_read_b64_tr_b8: the group's 8 tokens and 16 dims)
+  const int ve = (lane & 15) >> 1;
+  int v_off = kFp8 ? (8 * (ve >> 2) + 4 * g + (ve & 3)) * L::kPRowBytes + 16 * ((lane >> 4) & 1) +
+                         8 * (lane & 1)
+                   : (4 * g + ((lane & 15) >> 2)) * L::kPRowBytes + 32 * ((lane >> 4) & 1) +
+                         8 * (lane & 3);
   // one opaque per-lane offset: the loop adds the tile's slot to it once and every
   // transposed read takes its constant part in the instruction's offset field
   asm volatile("" : "+v"(v_off));
@@ -194,25 +181,42 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   // S^T of one tile: K fragments KA MFMAs ahead in a register ring; the order is pinned
   // by scheduling barriers (left alone, the scheduler issues each read right before
   // its MFMA and waits for it, exposing the LDS latency once per MFMA)
-  auto scores = [&](const uint16_t* buf) {
+  auto scores = [&](const uint8_t* buf) {
     f32x16 sc = {};
-    bf16x8 kb[KA + 1];
+    if constexpr (kFp8) {
+      // 16 codes per read, two k-steps each, widened exactly after the read
+      u32x4 kr[KA + 1];
 #pragma unroll
-    for (int kk = 0; kk < KA; ++kk) kb[kk] = *(const bf16x8*)(buf + a_off + 16 * kk);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int kk = 0; kk < kKSteps; ++kk) {
-      sc = mfma_32x32x16(kb[kk % (KA + 1)], qf[kk], sc);
-      if (kk + KA < kKSteps)
-        kb[(kk + KA) % (KA + 1)] = *(const bf16x8*)(buf + a_off + 16 * (kk + KA));
+      for (int j = 0; j < KA; ++j) kr[j] = *(const u32x4*)(buf + a_off + 32 * j);
       __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < kKSteps / 2; ++j) {
+        bf16x8 lo, hi;
+        fp8x16_to_bf16(kr[j % (KA + 1)], lo, hi);
+        if (j + KA < kKSteps / 2) kr[(j + KA) % (KA + 1)] = *(const u32x4*)(buf + a_off + 32 * (j + KA));
+        sc = mfma_32x32x16(lo, qf[2 * j], sc);
+        sc = mfma_32x32x16(hi, qf[2 * j + 1], sc);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+      bf16x8 kb[KA + 1];
+#pragma unroll
+      for (int kk = 0; kk < KA; ++kk) kb[kk] = *(const bf16x8*)(buf + a_off + 32 * kk);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 0; kk < kKSteps; ++kk) {
+        sc = mfma_32x32x16(kb[kk % (KA + 1)], qf[kk], sc);
+        if (kk + KA < kKSteps)
+          kb[(kk + KA) % (KA + 1)] = *(const bf16x8*)(buf + a_off + 32 * (kk + KA));
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     return sc;
   };
   // Each row's reference: its maximum over tile 0 (key 0 is visible to every row), set
   // once before the key loop from a score chain of its own, so the loop carries no
   // first-tile code.  The row's other 16 tokens sit in lane l ^ 32.
-  auto set_reference = [&](const uint16_t* buf) {
+  auto set_reference = [&](const uint8_t* buf) {
     const f32x16 sc = scores(buf);
     const int lim = tq - 4 * g;
     float cm = -INFINITY;
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
     m_ref = wave_max_xor32(cm);
   };
 
-  auto compute = [&](const uint16_t* buf, int kt) {
+  auto compute = [&](const uint8_t* buf, int kt) {
     {
       const f32x16 sc = scores(buf);
       // lane (n, g) holds tokens kt*32 + 8 (i/4) + 4 g + i%4 of row n.  Scores are
@@ -269,22 +273,40 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
       }
       // V^T operands VA MFMAs ahead in a register ring, pinned the same way; MFMA m
       // covers dims 32 (m / 2) .. + 31 and keys 16 (m % 2) .. + 15
-      auto vread = [&](int m) {
-        const uint16_t* src = buf + v_off + (16 * (m & 1)) * kPRow + 32 * (m >> 1);
-        const i16x4 lo = lds_read_tr16(src);
-        const i16x4 hi = lds_read_tr16(src + 8 * kPRow);
-        const i16x8 v8 = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        return __builtin_bit_cast(bf16x8, v8);
-      };
-      bf16x8 vb[VA + 1];
+      if constexpr (kFp8) {
+        // the ring holds the raw codes; each operand is widened at its MFMA
+        auto vread8 = [&](int m) {
+          return lds_read_tr8(buf + v_off + 16 * (m & 1) * L::kPRowBytes + 32 * (m >> 1));
+        };
+        u32x2 vr[VA + 1];
 #pragma unroll
-      for (int m = 0; m < VA; ++m) vb[m] = vread(m);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int m = 0; m < 32; ++m) {
-        acc[m >> 1] = mfma_32x32x16(vb[m % (VA + 1)], pf[m & 1], acc[m >> 1]);
-        if (m + VA < 32) vb[(m + VA) % (VA + 1)] = vread(m + VA);
+        for (int m = 0; m < VA; ++m) vr[m] = vread8(m);
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 32; ++m) {
+          const bf16x8 v = fp8x8_to_bf16(vr[m % (VA + 1)]);
+          if (m + VA < 32) vr[(m + VA) % (VA + 1)] = vread8(m + VA);
+          acc[m >> 1] = mfma_32x32x16(v, pf[m & 1], acc[m >> 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        auto vread = [&](int m) {
+          const uint8_t* src = buf + v_off + 16 * (m & 1) * L::kPRowBytes + 64 * (m >> 1);
+          const i16x4 lo = lds_read_tr16(src);
+          const i16x4 hi = lds_read_tr16(src + 8 * L::kPRowBytes);
+          const i16x8 v8 = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+          return __builtin_bit_cast(bf16x8, v8);
+        };
+        bf16x8 vb[VA + 1];
+#pragma unroll
+        for (int m = 0; m < VA; ++m) vb[m] = vread(m);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 32; ++m) {
+          acc[m >> 1] = mfma_32x32x16(vb[m % (VA + 1)], pf[m & 1], acc[m >> 1]);
+          if (m + VA < 32) vb[(m + VA) % (VA + 1)] = vread(m + VA);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
   };
@@ -294,50 +316,37 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
   for (int i = 0; i < 16; ++i) acc[i] = (f32x16){};
   l_run = 0.f;
   lb_run = 0.f;
-  if constexpr (kFp8) {
-    Fp8Stage st;
-    st.load(p.kv, seq_start, len, 0, tid);
-    st.store(lds, tid);
-    __syncthreads();
-    if (first_pass) set_reference(lds);
-    for (int kt = 0; kt < n_tiles; ++kt) {
-      const bool more = kt + 1 < n_tiles;
-      if (more) st.load(p.kv, seq_start, len, (kt + 1) * kTile, tid);
-      compute(lds + (kt & 1) * kTileElems, kt);
-      if (more) st.store(lds + ((kt + 1) & 1) * kTileElems, tid);
-      __syncthreads();
-    }
-  } else {
+  {
     // tile kt lives in slot kt % 4
     const uint32_t base = lds_addr(lds);
-    const uint8_t* seq_kv = p.kv + (size_t)seq_start * kRowBytes;
+    const uint8_t* seq_kv = p.kv + (size_t)seq_start * L::kRowBytes;
     // Byte offsets of this lane's ten chunks within a tile, fixed for the whole loop: a
     // tile that lies inside the sequence takes them as they are, its first row folded
     // into the scalar base; only the sequence's last, partial tile clamps rows.
-    uint32_t dma_off[kDmaPerWave];
+    uint32_t dma_off[L::kDmaPerWave];
 #pragma unroll
-    for (int i = 0; i < kDmaPerWave; ++i) {
-      const int pos = 64 * min(wave + 4 * i, kDmaBlocks - 1) + lane;
-      int row = pos / kPRowChunks, pc = pos - row * kPRowChunks;
+    for (int i = 0; i < L::kDmaPerWave; ++i) {
+      const int pos = 64 * min(wave + 4 * i, L::kDmaBlocks - 1) + lane;
+      int row = pos / L::kPRowChunks, pc = pos - row * L::kPRowChunks;
       if (row >= kTile) row = kTile - 1;
-      if (pc == kPRowChunks - 1) pc = 0;
-      dma_off[i] = (uint32_t)(row * kRowBytes + 16 * pc);
+      if (pc == L::kPRowChunks - 1) pc = 0;
+      dma_off[i] = (uint32_t)(row * L::kRowBytes + 16 * pc);
     }
     auto copy_tile = [&](int tok0, uint32_t slot) {
       if (tok0 + kTile <= len) {
-        const uint8_t* tile_kv = seq_kv + (size_t)tok0 * kRowBytes;
+        const uint8_t* tile_kv = seq_kv + (size_t)tok0 * L::kRowBytes;
 #pragma unroll
-        for (int i = 0; i < kDmaPerWave; ++i)
-          dma16(tile_kv, dma_off[i], slot + 1024 * min(wave + 4 * i, kDmaBlocks - 1));
+        for (int i = 0; i < L::kDmaPerWave; ++i)
+          dma16(tile_kv, dma_off[i], slot + 1024 * min(wave + 4 * i, L::kDmaBlocks - 1));
       } else {
-        dma_tile(seq_kv, len, tok0, slot, wave, lane);
+        dma_tile<kFp8>(seq_kv, len, tok0, slot, wave, lane);
       }
     };
     copy_tile(0, base);
-    if (n_tiles > 1) copy_tile(kTile, base + kSlotBytes);
+    if (n_tiles > 1) copy_tile(kTile, base + L::kSlotBytes);
     if (first_pass) {
       if (n_tiles > 1)
-        wait_vmcnt<kDmaPerWave>();  // this wave's copies of tile 0 have landed
+        wait_vmcnt<L::kDmaPerWave>();  // this wave's copies of tile 0 have landed
       else
         wait_vmcnt<0>();
       __syncthreads();
@@ -351,10 +360,10 @@ __global__ __launch_bounds__(256, 1) void prefill_kernel(const PrefillParams p) 
       if ((kt & 1) == 0) {
         wait_vmcnt<0>();
         __syncthreads();
-        if (kt + 2 < n_tiles) copy_tile((kt + 2) * kTile, base + ((kt + 2) % kRing) * kSlotBytes);
-        if (kt + 3 < n_tiles) copy_tile((kt + 3) * kTile, base + ((kt + 3) % kRing) * kSlotBytes);
+        if (kt + 2 < n_tiles) copy_tile((kt + 2) * kTile, base + ((kt + 2) % kRing) * L::kSlotBytes);
+        if (kt + 3 < n_tiles) copy_tile((kt + 3) * kTile, base + ((kt + 3) % kRing) * L::kSlotBytes);
       }
-      compute(lds + (kt % kRing) * (kSlotBytes / 2), kt);
+      compute(lds + (kt % kRing) * L::kSlotBytes, kt);
     }
   }
   // a row beyond its cap anywhere in the work-group: all waves run the loop again
