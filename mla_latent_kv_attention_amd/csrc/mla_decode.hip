@@ -395,7 +395,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     // whatever the rows past a sequence's end hold never reaches the arithmetic.
     // Rows are 592 bytes apart and a pair's second stage starts 128 bytes (mod 256)
     // after the first: the 16 fragment reads of a 16-lane phase fall in 16 distinct
-    // 16-byte bank groups, and a transposed read's 32 rows in distinct banks.
+    // 16-byte bank groups, and each 32-lane half of a transposed read (16 rows, 8 from
+    // each stage) in distinct banks.
     uint8_t* const stA = sm.st[wave];
     uint8_t* const stB = stA + kStageB;
     // A prefetch past the wave's last step (live false) still issues its loads, so the
@@ -479,9 +480,9 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
     constexpr int kStride = kStep * kWaves;
     const int t_first = sr.base + kStep * (a + wave);
     const int n_steps = a + wave < e ? (e - a - wave + kWaves - 1) / kWaves : 0;
-    // Every iteration issues the same loads (prefetches past the wave's last step
-    // re-read that step), so the compiler counts them exactly and keeps the ring in
-    // flight.
+    // Every iteration issues the same loads (a prefetch past the wave's last step
+    // re-reads that step, or for FP8 one 16-byte piece of it), so the compiler counts
+    // them exactly and keeps the ring in flight.
     u32x4 ring[kDepth][kLoads];
     const int last_t0 = t_first + (n_steps - 1) * kStride;
     auto step_t0 = [&](int i) { return min(t_first + i * kStride, last_t0); };
