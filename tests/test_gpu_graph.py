@@ -48,6 +48,10 @@ def test_graph_replay_of_every_entry_point(mla):
     pd = mi.prefill_inputs(mi.PrefillWorkload("graph", [150, 41], 12, "bf16", seed=7102))
     pq, pkv, pcu = bf16_tensor(pd["q"], DEV), bf16_tensor(pd["kv"], DEV), i32(pd["cu_seqlens"], DEV)
     ref_po, ref_pl = oracle.prefill(pd["q"], pd["kv"], False, 1.0, pd["cu_seqlens"], SIGMA)
+    # the same prefill over an FP8 cache (its tiles staged in LDS as codes)
+    pd8 = mi.prefill_inputs(mi.PrefillWorkload("graph8", [150, 41], 12, "fp8", seed=7105))
+    pq8, pkv8, pcu8 = bf16_tensor(pd8["q"], DEV), torch.from_numpy(pd8["kv"]).to(DEV), i32(pd8["cu_seqlens"], DEV)
+    ref_po8, ref_pl8 = oracle.prefill(pd8["q"], pd8["kv"], True, pd8["kv_scale"], pd8["cu_seqlens"], SIGMA)
     # merge: 6 partials of 40 rows, one row with no keys anywhere
     rng = np.random.default_rng(7103)
     po_np = rng.standard_normal((6, 40, 512)).astype(np.float32)
@@ -63,6 +67,8 @@ def test_graph_replay_of_every_entry_point(mla):
                                            kv_scale=cache.kv_scale, max_kv_len=2100,
                                            num_splits=s, workspace=ws[s])
         r["prefill"] = mla.prefill(pq, pkv, pcu, softmax_scale=SIGMA, max_seqlen=150)
+        r["prefill8"] = mla.prefill(pq8, pkv8, pcu8, softmax_scale=SIGMA, kv_scale=pd8["kv_scale"],
+                                    max_seqlen=150)
         r["merge"] = mla.merge_lse(po, pl)
         return r
 
@@ -73,6 +79,8 @@ def test_graph_replay_of_every_entry_point(mla):
             check_lse(l, ref_vl, "%s verify (%d pieces) lse" % (what, s))
         check_out(r["prefill"][0], ref_po, what + " prefill out")
         check_lse(r["prefill"][1], ref_pl, what + " prefill lse")
+        check_out(r["prefill8"][0], ref_po8, what + " fp8 prefill out")
+        check_lse(r["prefill8"][1], ref_pl8, what + " fp8 prefill lse")
         check_out(r["merge"][0], ref_mo, what + " merge out")
         check_lse(r["merge"][1], ref_ml, what + " merge lse")
 
