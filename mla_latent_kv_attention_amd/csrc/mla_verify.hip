@@ -522,12 +522,13 @@ __global__ __launch_bounds__(256, 1) void verify_kernel(const DecodeParams p) {
             store_agent16(rsrc, (uint32_t)(rr * kDV + dv0 + 16 * mt + 4 * grp) * 4,
                           acc[rb][mt] * inv);
         }
-      } else {  // read by the merge launch that follows: plain stores
+      } else {  // read once by the merge launch that follows: plain stores, nontemporal
         if (wave == 0 && grp == 0) p.part_lse[slot_rows + rr] = lse_v;
         if (l > 0.f) {
           float* dst = p.part_out + (slot_rows + rr) * kDV + dv0 + 4 * grp;
 #pragma unroll
-          for (int mt = 0; mt < kDvWave / 16; ++mt) *(f32x4*)(dst + 16 * mt) = acc[rb][mt] * inv;
+          for (int mt = 0; mt < kDvWave / 16; ++mt)
+            __builtin_nontemporal_store(acc[rb][mt] * inv, (f32x4*)(dst + 16 * mt));
         }
       }
     }
