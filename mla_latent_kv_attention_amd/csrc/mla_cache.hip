@@ -13,7 +13,9 @@
 // One thread per 16-value chunk of a row (36 chunks per row): two 16-byte loads
 // of BF16, one 16-byte store of FP8 codes (or two of BF16).  Consecutive threads
 // take consecutive chunks, so a wave reads and writes contiguous runs.  The op is
-// HBM-bound: 1,152 bytes in and 576 (FP8) or 1,152 (BF16) bytes out per row.
+// HBM-bound: 1,152 bytes in and 576 (FP8) or 1,152 (BF16) bytes out per row.  The
+// stores carry the nontemporal hint (32,768 rows into an FP8 cache: 13.8 -> 13.0 us;
+// on the loads the hint was slower).
 #include <cmath>
 
 #include "mla_device.h"
@@ -96,11 +98,11 @@ __global__ __launch_bounds__(256) void cache_write_kernel(const uint16_t* __rest
       }
       out[q] = word;
     }
-    *(u32x4*)(kv + s * kDK + 16 * c) = out;
+    __builtin_nontemporal_store(out, (u32x4*)(kv + s * kDK + 16 * c));
   } else {
     uint16_t* dst = (uint16_t*)kv + s * kDK + 16 * c;
-    *(u32x4*)dst = lo;
-    *(u32x4*)(dst + 8) = hi;
+    __builtin_nontemporal_store(lo, (u32x4*)dst);
+    __builtin_nontemporal_store(hi, (u32x4*)(dst + 8));
   }
 }
 
