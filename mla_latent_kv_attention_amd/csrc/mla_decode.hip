@@ -661,8 +661,8 @@ __global__ __launch_bounds__(256, 1) void decode_kernel(const DecodeParams p) {
 // running maximum; the groups' results meet in LDS.  kQ = 4 takes a row's shares in a
 // quarter of the rounds, for sequences spread over many pieces (one long sequence);
 // kQ = 1 launches a quarter of the work-groups, for many rows with few shares each.
-// The decode launch that wrote the shares has completed, so plain loads see them (each
-// share is read once: nontemporal loads).  A
+// The decode launch that wrote the shares has completed, so plain loads see them (the
+// nontemporal hint on them cost the 1,024-key decode 1 us, and gained nothing elsewhere).  A
 // share that saw no key of the row has lse = -inf and an unwritten row, which its
 // zero weight selects away.
 template <int kQ>
@@ -698,7 +698,7 @@ __global__ __launch_bounds__(256) void merge_shares_kernel(const DecodeParams p)
         const f32x4* src =
             (const f32x4*)(p.part_out + ((size_t)(v + b) * R + rr) * kDV + d0 + 4 * kVec * l);
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) t[u][k] = __builtin_nontemporal_load(src + k);
+        for (int k = 0; k < kVec; ++k) t[u][k] = src[k];
       }
     }
     float m_new = mx;
