@@ -447,9 +447,10 @@ def secondary_configs(torch, mi, mla, acc, oracle, bf16_tensor, cache_to_device,
 
 
 def time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev, stream,
-                 pw, steps):
-    """One causal prefill workload: parity on sampled tokens against the oracle, then the
-    mean of `steps` HIP-event-timed calls."""
+                 pw, steps, warmup=4):
+    """One causal prefill workload: parity on sampled tokens against the oracle, `warmup`
+    untimed calls (the GPU idles while the oracle runs, and its clocks take about three
+    11 ms calls to come back up), then the mean of `steps` HIP-event-timed calls."""
     log("generating", pw.name)
     pd = mi.prefill_inputs(pw)
     T = pw.total_tokens
@@ -475,7 +476,8 @@ def time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse,
     ti = torch.from_numpy(toks).to(dev)
     check_out(pout[ti], ro, pw.name + " out")
     check_lse(plse[ti], rl, pw.name + " lse")
-    pstep()
+    for _ in range(max(1, warmup)):
+        pstep()
     pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
     torch.cuda.synchronize()
@@ -503,7 +505,7 @@ def run_prefill(args, torch, mi, mla, acc, oracle, bf16_tensor, check_out, check
     the oracle's rate on a bounded sample of the same workload."""
     pw = mi.WORKLOADS[PREFILL_WORKLOAD]
     res = time_prefill(torch, mi, mla, acc, oracle, bf16_tensor, check_out, check_lse, dev,
-                       stream, pw, args.prefill_steps)
+                       stream, pw, args.prefill_steps, args.prefill_warmup)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on prefill tokens")
         res["cpu_baseline"] = prefill_cpu_baseline(mi.prefill_inputs(pw), pw)
@@ -591,7 +593,9 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # ~10 ms of decode steps: after the parity check's CPU work the GPU's clocks take a
+    # few milliseconds of sustained work to come back up
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=3, help="KV pool copies cycled over")
     ap.add_argument("--num-splits", type=int, default=0, help="pieces; 0 = automatic plan")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -601,6 +605,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true",
                     help="prefill figures only (for profiling the prefill kernel)")
     ap.add_argument("--prefill-steps", type=int, default=5)
+    ap.add_argument("--prefill-warmup", type=int, default=4)
     ap.add_argument("--secondary", default="",
                     help="comma-separated secondary workloads to run (default: all)")
     ap.add_argument("--timeline", action="store_true",
