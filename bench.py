@@ -592,7 +592,7 @@ def run_timeline(args, torch, mi, mla, bf16_tensor, cache_to_device, dev):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     # ~10 ms of decode steps: after the parity check's CPU work the GPU's clocks take a
     # few milliseconds of sustained work to come back up
     ap.add_argument("--warmup", type=int, default=200)
