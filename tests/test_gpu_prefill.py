@@ -7,7 +7,8 @@ Small packed batches (every row checked) cover ragged sequence lengths around th
 configuration, over a BF16 and an FP8 cache, and is checked on one token of every
 128-row work-group block.  Invariants: prefill row i equals
 decode on the prefix of length i + 1, future keys do not matter, runs are bitwise
-repeatable.
+repeatable, and power-of-two scalings of q, the softmax scale and the FP8 scale move the
+results exactly (bitwise).
 """
 import numpy as np
 import pytest
@@ -99,6 +100,43 @@ def test_prefill_row_equals_decode_on_prefix(mla):
         check_lse(l[0], ref_l[k])
         check_lse(lse[i], ref_l[k])
         assert (o[0] - out[i]).abs().max().item() <= 1e-2
+
+
+def scaled_bf16_bits(bits: np.ndarray, c: float) -> np.ndarray:
+    """BF16 bit patterns multiplied by a power of two c (exact for these magnitudes)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32) * np.float32(c)
+    out = mi.to_bf16_bits(f)
+    assert np.array_equal((out.astype(np.uint32) << 16).view(np.float32), f)
+    return out
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_power_of_two_scale_invariants(mla, kv_dtype):
+    """The scores depend on q and the softmax scale only through their product, and an
+    FP8 cache's values through code x kv_scale: (q * c, scale / c) gives bitwise the same
+    out and lse for a power of two c, and (kv_scale * c, scale / c) gives out * c and the
+    same lse."""
+    d = mi.prefill_inputs(mi.PrefillWorkload("scale", [300, 45, 129], 12, kv_dtype, seed=3210))
+    q, kv, cu = d["q"], kv_tensor(d["kv"], kv_dtype), i32(d["cu_seqlens"], DEV)
+
+    def run(q_bits, scale, kv_scale):
+        o, l = mla.prefill(bf16_tensor(q_bits, DEV), kv, cu, softmax_scale=scale,
+                           kv_scale=kv_scale, out_dtype=torch.float32, max_seqlen=300)
+        torch.cuda.synchronize()
+        return o, l
+    base_o, base_l = run(q, SIGMA, d["kv_scale"])
+    for c in (2.0, 0.25):
+        print("case q x", c, kv_dtype, flush=True)
+        o, l = run(scaled_bf16_bits(q, c), SIGMA / c, d["kv_scale"])
+        assert torch.equal(o, base_o) and torch.equal(l, base_l)
+    if kv_dtype == "fp8":
+        for c in (4.0, 0.5):
+            print("case kv_scale x", c, flush=True)
+            o, l = run(q, SIGMA / c, d["kv_scale"] * c)
+            assert torch.equal(o, base_o * c) and torch.equal(l, base_l)
+    ref_o, ref_l = run_oracle(d, kv_dtype)
+    check_out(base_o, ref_o)
+    check_lse(base_l, ref_l)
 
 
 def test_future_keys_do_not_matter_and_runs_repeat(mla):
