@@ -7,8 +7,9 @@ Small packed batches (every row checked) cover ragged sequence lengths around th
 configuration, over a BF16 and an FP8 cache, and is checked on one token of every
 128-row work-group block.  Invariants: prefill row i equals
 decode on the prefix of length i + 1, future keys do not matter, runs are bitwise
-repeatable, and power-of-two scalings of q, the softmax scale and the FP8 scale move the
-results exactly (bitwise).
+repeatable, power-of-two scalings of q, the softmax scale and the FP8 scale move the
+results exactly, and repeated heads, zero-padded heads and reordered sequences leave every
+row unchanged (all bitwise).
 """
 import numpy as np
 import pytest
@@ -134,6 +135,52 @@ def test_power_of_two_scale_invariants(mla, kv_dtype):
             print("case kv_scale x", c, flush=True)
             o, l = run(q, SIGMA / c, d["kv_scale"] * c)
             assert torch.equal(o, base_o * c) and torch.equal(l, base_l)
+    ref_o, ref_l = run_oracle(d, kv_dtype)
+    check_out(base_o, ref_o)
+    check_lse(base_l, ref_l)
+
+
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+def test_heads_repeated_padded_and_sequences_reordered_are_bitwise_invariant(mla, kv_dtype):
+    """Each (token, head) row is computed on its own whatever rows share its
+    work-group, and key tiles start at the sequence's first token: 8 heads repeated
+    into 16 (both copies of every head), 12 heads zero-padded to 16 (K2.5 blog, section
+    "PR #35850 修复了什么": head counts per rank of 8, 12 and 16), and the packed
+    sequences in another order all give the same rows, bitwise."""
+    lens = [130, 1, 77, 256]
+    T = sum(lens)
+
+    def run(q_bits, kv_rows, cu, H, kv_scale):
+        o, l = mla.prefill(bf16_tensor(q_bits, DEV), kv_tensor(kv_rows, kv_dtype), i32(cu, DEV),
+                           softmax_scale=SIGMA, kv_scale=kv_scale, out_dtype=torch.float32,
+                           max_seqlen=max(lens))
+        torch.cuda.synchronize()
+        assert o.shape == (T, H, 512)
+        return o, l
+    d = mi.prefill_inputs(mi.PrefillWorkload("inv", lens, 8, kv_dtype, seed=3220))
+    base_o, base_l = run(d["q"], d["kv"], d["cu_seqlens"], 8, d["kv_scale"])
+    print("case repeated heads", kv_dtype, flush=True)
+    q16 = np.repeat(d["q"], 2, axis=1)  # heads h, h, h + 1, h + 1, ...
+    o16, l16 = run(q16, d["kv"], d["cu_seqlens"], 16, d["kv_scale"])
+    for c in range(2):
+        assert torch.equal(o16[:, c::2], base_o) and torch.equal(l16[:, c::2], base_l)
+    print("case reordered sequences", kv_dtype, flush=True)
+    order = [3, 0, 2, 1]
+    starts = np.asarray(d["cu_seqlens"][:-1])
+    tok = np.concatenate([np.arange(starts[b], starts[b] + lens[b]) for b in order])
+    cu_r = np.zeros(len(lens) + 1, np.int32)
+    cu_r[1:] = np.cumsum([lens[b] for b in order])
+    o_r, l_r = run(np.ascontiguousarray(d["q"][tok]), np.ascontiguousarray(d["kv"][tok]), cu_r,
+                   8, d["kv_scale"])
+    inv = torch.from_numpy(np.argsort(tok)).to(DEV)
+    assert torch.equal(o_r[inv], base_o) and torch.equal(l_r[inv], base_l)
+    print("case zero-padded heads", kv_dtype, flush=True)
+    d12 = mi.prefill_inputs(mi.PrefillWorkload("inv12", lens, 12, kv_dtype, seed=3221))
+    o12, l12 = run(d12["q"], d12["kv"], d12["cu_seqlens"], 12, d12["kv_scale"])
+    qpad = np.zeros((T, 16, 576), d12["q"].dtype)
+    qpad[:, :12] = d12["q"]
+    op, lp = run(qpad, d12["kv"], d12["cu_seqlens"], 16, d12["kv_scale"])
+    assert torch.equal(op[:, :12], o12) and torch.equal(lp[:, :12], l12)
     ref_o, ref_l = run_oracle(d, kv_dtype)
     check_out(base_o, ref_o)
     check_lse(base_l, ref_l)
